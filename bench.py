@@ -1,0 +1,214 @@
+"""Benchmark: GEMM TFLOP/s at M = N = K = 4096 and fraction of the MI355X
+matrix-core peak, on one GPU.
+
+A step is one C = A*B call of the library (global -> LDS staging, the LDS ring,
+the swizzled layout, the matrix-instruction loop and the epilogue all run inside
+that one kernel) on inputs already resident in HBM.  The headline line is the
+bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
+fp32-input 4096^3 products are measured the same way and reported under
+"per_dtype".
+
+    python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
+                    [--no-cpu-baseline] [--no-per-dtype]
+    python bench.py --copy-calibration      # plain copy of known size, for HBM counters
+
+Only one GPU is used; --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at M=N=K=4096 bf16/fp16/fp32 and % of MI355X MFMA peak"
+# MI355X published dense matrix peaks, TFLOP/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+WORKLOAD_FOR = {"bf16": "bf16_4096", "f16": "f16_4096", "f32": "f32_4096"}
+DESCRIPTION = {
+    "bf16_4096": "bf16 GEMM M=N=K=4096, row-major A and B, normal(0,1) inputs, fp32 accumulate, fp32 C",
+    "f16_4096": "fp16 GEMM M=N=K=4096, row-major A and B, uniform[-1,1] inputs, fp32 accumulate, fp16 C",
+    "f32_4096": "fp32 GEMM M=N=K=4096, row-major A and B, uniform[-1,1] inputs, fp32 accumulate, fp32 C",
+}
+KERNEL_SOURCE = os.path.join(ROOT, "dense_gemm_matrix_amd", "csrc", "dgemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """Floating-point operations of one product: one multiply and one add per term."""
+    return 2 * M * N * K
+
+
+def tflops(M: int, N: int, K: int, seconds: float) -> float:
+    return gemm_flops(M, N, K) / seconds / 1e12
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    v = fields.get(f"{workload}_hbm_bytes_per_launch")
+    return float(v) if v else None
+
+
+def device_inputs(name):
+    import torch
+    from synth_inputs import to_torch, torch_dtype, workload
+    A, B, meta = workload(name)
+    Ad = to_torch(A, meta["dtype"]).to("cuda")
+    Bd = to_torch(B, meta["dtype"]).to("cuda")
+    Cd = torch.empty((meta["M"], meta["N"]), dtype=torch_dtype(meta["out"]), device="cuda")
+    return A, B, Ad, Bd, Cd, meta
+
+
+def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int):
+    """Average kernel duration (s) over `steps` back-to-back launches, timed with
+    HIP events recorded on the stream the library launches on."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        entry(Ad, Bd, Cd, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        entry(Ad, Bd, Cd, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) * 1e-3 / steps, wall
+
+
+def cpu_baseline(A, B, meta, target_s: float = 12.0):
+    """The oracle, untuned, on a bounded sample of the same product: the first
+    r rows of C, r chosen so the timed run takes about target_s seconds."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    dt = meta["dtype"]
+    probe = min(meta["M"], max(threads, 8))
+    t0 = time.perf_counter()
+    oracle.gemm(dt, A, B, rows=np.arange(probe), nthreads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(meta["M"], max(probe, probe * target_s / max(t_probe, 1e-3))))
+    rows = max(threads, rows // threads * threads)
+    t0 = time.perf_counter()
+    oracle.gemm(dt, A, B, rows=np.arange(rows), nthreads=threads)
+    t = time.perf_counter() - t0
+    return {"value": round(tflops(rows, meta["N"], meta["K"], t), 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C ({rows}x{meta['N']} outputs, K={meta['K']}) of the "
+                      f"{meta['name']} product, fp64 triple loop incl. exact widening of B, "
+                      f"{t:.1f} s"}
+
+
+def copy_calibration(gib: float = 1.0, reps: int = 5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default="bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-dtype", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this GEMM engine has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_matrix_amd as dg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    entry = {"bf16": dg.gemm_bf16, "f16": dg.gemm_f16, "f32": dg.gemm_f32}
+    name = WORKLOAD_FOR[args.dtype]
+    print(f"bench: preparing {name}", file=sys.stderr, flush=True)
+    A, B, Ad, Bd, Cd, meta = device_inputs(name)
+    M, N, K = meta["M"], meta["N"], meta["K"]
+    torch.cuda.synchronize()
+    print(f"bench: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    per_launch, wall = time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, args.warmup)
+    value = tflops(M, N, K, per_launch)
+    peak = PEAK_TFLOPS[args.dtype]
+    traffic = measured_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_launch * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTION[name], "M": M, "N": N, "K": K,
+                   "frac_of_peak": round(value / peak, 4), "wall_s_timed_region": round(wall, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(value / peak, 4), "traffic": traffic},
+    }
+    if not args.no_per_dtype:
+        per = {}
+        for dt in ("bf16", "f16", "f32"):
+            if dt == args.dtype:
+                continue
+            wn = WORKLOAD_FOR[dt]
+            print(f"bench: per-dtype {wn}", file=sys.stderr, flush=True)
+            _, _, a2, b2, c2, m2 = device_inputs(wn)
+            steps = max(10, args.steps // (8 if dt == "f32" else 1))
+            t2, _ = time_gemm(entry[dt], a2, b2, c2, steps, max(3, args.warmup // 4))
+            v2 = tflops(m2["M"], m2["N"], m2["K"], t2)
+            per[dt] = {"workload": DESCRIPTION[wn], "value": round(v2, 2), "unit": "TFLOP/s",
+                       "ms_per_launch": round(t2 * 1e3, 5), "steps": steps,
+                       "frac_of_peak": round(v2 / PEAK_TFLOPS[dt], 4), "peak": PEAK_TFLOPS[dt]}
+            del a2, b2, c2
+        line["per_dtype"] = per
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(A, B, meta)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

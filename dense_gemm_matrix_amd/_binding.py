@@ -1,0 +1,151 @@
+"""ctypes binding of libdgemm.so: the C ABI of include/dgemm.h, by the same names.
+
+This layer only marshals arguments: it reads shapes, row pitches and data
+pointers from torch tensors and passes them, with the tensor's current HIP
+stream, to the library.  Every arithmetic step runs in the library's kernels.
+There is no fallback: if libdgemm.so is missing or fails to load, importing
+this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "or python -m dense_gemm_matrix_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_c_int, _c_void_p = ctypes.c_int, ctypes.c_void_p
+_lib.gemm_f32.argtypes = [_c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_int,
+                          _c_void_p, _c_int, _c_void_p]
+for _f in (_lib.gemm_bf16, _lib.gemm_f16):
+    _f.argtypes = [_c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_int,
+                   _c_void_p, _c_int, _c_int, _c_void_p]
+for _f in (_lib.gemm_f32, _lib.gemm_bf16, _lib.gemm_f16):
+    _f.restype = _c_int
+_lib.dgemm_status_string.argtypes = [_c_int]
+_lib.dgemm_status_string.restype = ctypes.c_char_p
+_P = ctypes.POINTER(ctypes.c_int)
+_lib.dgemm_tile_map.argtypes = [_c_int, _c_int, _c_int, _c_int, _P, _P, _P, _P, _P]
+_lib.dgemm_tile_map.restype = _c_int
+
+DGEMM_OK = 0
+DGEMM_ERR_INVALID_VALUE = 1
+DGEMM_ERR_LEADING_DIM = 2
+DGEMM_ERR_MISALIGNED = 3
+DGEMM_ERR_ALIAS = 4
+DGEMM_ERR_TOO_LARGE = 5
+DGEMM_ERR_DEVICE = 6
+DGEMM_ERR_LAUNCH = 7
+DGEMM_OUT_F32 = 0
+DGEMM_OUT_SAME = 1
+IN_CODES = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+class DgemmError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(dgemm_status_string(status))
+
+
+def dgemm_status_string(status: int) -> str:
+    return _lib.dgemm_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != DGEMM_OK:
+        raise DgemmError(status)
+
+
+def _pitch(t: torch.Tensor, row_len: int) -> int:
+    """Row pitch in elements.  A matrix with at most one row never steps to a
+    second row, so its pitch is free: it is given as the row length rounded up
+    to 16 bytes, which the ABI's alignment rule accepts."""
+    if t.dim() != 2:
+        raise ValueError("operands must be 2-D")
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("operands must be row-major with unit inner stride")
+    if t.shape[0] > 1:
+        return int(t.stride(0))
+    per16 = 16 // t.element_size()
+    return (max(row_len, 1) + per16 - 1) // per16 * per16
+
+
+def _shapes(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or tuple(C.shape) != (M, N):
+        raise ValueError(f"shapes {tuple(A.shape)} x {tuple(B.shape)} -> {tuple(C.shape)}")
+    for t in (A, B, C):
+        if t.device.type != "cuda":
+            raise ValueError("operands must be device tensors")
+    return M, N, K
+
+
+def _stream(C: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gemm_f32(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> None:
+    """C = A @ B for fp32 A [M,K], B [K,N], C [M,N]; enqueued on `stream`."""
+    M, N, K = _shapes(A, B, C)
+    if not (A.dtype == B.dtype == C.dtype == torch.float32):
+        raise TypeError("gemm_f32 takes float32 A, B and C")
+    with torch.cuda.device(C.device):
+        _check(_lib.gemm_f32(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(), _pitch(B, N),
+                             C.data_ptr(), _pitch(C, N), _stream(C, stream)))
+
+
+def _gemm16(fn, dtype, A, B, C, stream):
+    M, N, K = _shapes(A, B, C)
+    if A.dtype != dtype or B.dtype != dtype:
+        raise TypeError(f"inputs must be {dtype}")
+    if C.dtype == torch.float32:
+        out = DGEMM_OUT_F32
+    elif C.dtype == dtype:
+        out = DGEMM_OUT_SAME
+    else:
+        raise TypeError(f"C must be float32 or {dtype}")
+    with torch.cuda.device(C.device):
+        _check(fn(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(), _pitch(B, N),
+                  C.data_ptr(), _pitch(C, N), out, _stream(C, stream)))
+
+
+def gemm_bf16(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> None:
+    """C = A @ B for bf16 A, B; C is float32 or bfloat16 (rounded once, nearest even)."""
+    _gemm16(_lib.gemm_bf16, torch.bfloat16, A, B, C, stream)
+
+
+def gemm_f16(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> None:
+    """C = A @ B for fp16 A, B; C is float32 or float16 (rounded once, nearest even)."""
+    _gemm16(_lib.gemm_f16, torch.float16, A, B, C, stream)
+
+
+_ENTRY = {torch.float32: gemm_f32, torch.bfloat16: gemm_bf16, torch.float16: gemm_f16}
+
+
+def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, stream=None) -> torch.Tensor:
+    """Allocates C (torch allocator) and computes C = A @ B with the library."""
+    if out_dtype is None:
+        out_dtype = A.dtype
+    C = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype, device=A.device)
+    _ENTRY[A.dtype](A, B, C, stream)
+    return C
+
+
+def dgemm_tile_map(M: int, N: int, in_fmt: str, wg: int = -1) -> dict:
+    """Host query of the workgroup -> tile mapping (no GPU needed)."""
+    v = [ctypes.c_int(-1) for _ in range(5)]
+    _check(_lib.dgemm_tile_map(M, N, IN_CODES[in_fmt], wg, *[ctypes.byref(x) for x in v]))
+    return {"tile_rows": v[0].value, "tile_cols": v[1].value, "num_wg": v[2].value,
+            "tile_m": v[3].value, "tile_n": v[4].value}
+
+
+def raw():
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib

@@ -1,0 +1,119 @@
+/*
+ * dgemm.h -- dense GEMM C = A*B on AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (both pages' kernels and the nine-levels tutorial's naive
+ * kernel compute exactly this; see the sgemm tf32 page "[CUDA 优化实战] sgemm
+ * tf32 - 超越 cuBLAS" section 2, the hgemm page "[CUDA 优化实战] hgemm - 超越
+ * cuBLAS" section 1, and "CUDA GEMM优化九重天" section 2.1):
+ *
+ *     C[i][j] = sum_{k<K} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ *
+ * A is row-major M x K with row pitch lda elements, B is row-major K x N with
+ * row pitch ldb, C is row-major M x N with row pitch ldc.  Products are
+ * accumulated in fp32 (the pages' matrix instructions all accumulate in fp32).
+ * C is overwritten; there is no alpha/beta.  Elements of C outside the M x N
+ * window (the ldc - N gap of each row) are never written.
+ *
+ * Ownership: A, B and C are DEVICE pointers owned by the caller.  The library
+ * allocates no device memory and keeps no pointer after a call returns.
+ *
+ * Execution: each call validates its arguments, enqueues one kernel on
+ * `stream` (a hipStream_t; NULL means the default stream) and returns without
+ * waiting.  Results are visible once the stream has synchronised.  Calls from
+ * different host threads on different streams are independent.
+ *
+ * Errors: a non-zero status is returned and NOTHING is enqueued when the
+ * arguments are invalid; C is left untouched.  The library never aborts and
+ * keeps no error state beyond the return value.
+ *
+ * Preconditions (the tutorial's advice in section 6.5 on 16-byte aligned,
+ * row-major operands, which this library makes a rule):
+ *   - A, B and C are 16-byte aligned, and every row pitch in bytes
+ *     (lda*esize_in, ldb*esize_in, ldc*esize_out) is a multiple of 16;
+ *   - lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N);
+ *   - C's bytes overlap neither A's nor B's.
+ * Edge semantics: M == 0 or N == 0 is a no-op; K == 0 writes C = 0 (the empty
+ * sum).  Any M, N, K >= 0 is accepted; tiles at the matrix edges read zeros
+ * beyond K and never store beyond M or N.
+ */
+#ifndef DGEMM_H
+#define DGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DGEMM_OK = 0,
+    DGEMM_ERR_INVALID_VALUE = 1, /* negative M/N/K, NULL pointer with nonzero extent, bad `out` */
+    DGEMM_ERR_LEADING_DIM = 2,   /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N)           */
+    DGEMM_ERR_MISALIGNED = 3,    /* a base pointer or a row pitch in bytes not a multiple of 16   */
+    DGEMM_ERR_ALIAS = 4,         /* C's byte range overlaps A's or B's                           */
+    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 128*ldb bytes reach 2 GiB (32-bit offsets)  */
+    DGEMM_ERR_DEVICE = 6,        /* no current device, or it is not a gfx950                     */
+    DGEMM_ERR_LAUNCH = 7         /* the kernel launch reported an error                          */
+} dgemm_status;
+
+/* Format of C for the 16-bit entry points. */
+typedef enum {
+    DGEMM_OUT_F32 = 0,  /* C is fp32: the accumulator itself                          */
+    DGEMM_OUT_SAME = 1  /* C has the input format, rounded once, to nearest even       */
+} dgemm_out;
+
+/*
+ * fp32 inputs, fp32 C.  gfx950 has no reduced-precision (xf32) matrix
+ * instruction, so products use the full-fp32 matrix instruction
+ * v_mfma_f32_32x32x2_f32: the sgemm tf32 page's workload (section 0, M = N =
+ * K = 4096 fp32) without its tf32 input truncation.
+ */
+int gemm_f32(int M, int N, int K,
+             const float* A, int lda,
+             const float* B, int ldb,
+             float* C, int ldc,
+             void* stream);
+
+/*
+ * bf16 inputs (raw 16-bit storage), fp32 accumulation, C fp32 (out =
+ * DGEMM_OUT_F32) or bf16 (out = DGEMM_OUT_SAME).  The hgemm page's workload
+ * (section 0, M = N = K = 4096, bf16 in and out).
+ */
+int gemm_bf16(int M, int N, int K,
+              const void* A, int lda,
+              const void* B, int ldb,
+              void* C, int ldc,
+              int out,
+              void* stream);
+
+/* fp16 inputs; otherwise as gemm_bf16 (the hgemm page covers both formats). */
+int gemm_f16(int M, int N, int K,
+             const void* A, int lda,
+             const void* B, int ldb,
+             void* C, int ldc,
+             int out,
+             void* stream);
+
+/* A static, NUL-terminated description of a status code (never NULL). */
+const char* dgemm_status_string(int status);
+
+/*
+ * Host-side query of the kernel's work distribution, for tests and tuning; it
+ * launches nothing and needs no GPU.  For a problem of M x N outputs and input
+ * format `in` (0 = fp32, 1 = bf16, 2 = fp16), writes the macro-tile shape and
+ * the number of workgroups, and, when wg is in [0, *num_wg), the output tile
+ * (row block *tile_m, column block *tile_n) that workgroup `wg` computes.  The
+ * mapping is a bijection from workgroups to tiles: it first gives each of the
+ * 8 XCDs a contiguous run of tiles (workgroups are dispatched to XCDs in turn),
+ * then walks each run in column strips a few tile rows high so that
+ * neighbouring workgroups share A and B panels in L2 (the sgemm tf32 page's
+ * "Grid Swizzling", section 4).  Any output pointer may be NULL.
+ * Returns DGEMM_OK, or DGEMM_ERR_INVALID_VALUE for negative sizes or a bad `in`.
+ */
+int dgemm_tile_map(int M, int N, int in, int wg,
+                   int* tile_rows, int* tile_cols, int* num_wg,
+                   int* tile_m, int* tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGEMM_H */

@@ -74,3 +74,16 @@ def workload(name: str):
     A, B = pair(M, N, K, dist, dtype, seed)
     return A, B, {"name": name, "dtype": dtype, "M": M, "N": N, "K": K,
                   "dist": dist, "seed": seed, "out": out}
+
+
+def to_torch(x: np.ndarray, dtype: str):
+    """A storage array as a CPU torch tensor of the matching dtype (no copy of values)."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]

@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, rejects invalid arguments before touching a device, and its
+workgroup -> tile map is a bijection.  No kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_gemm_matrix_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|char|void)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("gemm_f32", "gemm_bf16", "gemm_f16", "dgemm_status_string", "dgemm_tile_map"):
+        assert want in names
+
+
+def test_library_exports_every_declared_function():
+    lib = dg.raw()
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    seen = set()
+    for s in range(8):
+        msg = dg.dgemm_status_string(s)
+        assert msg.startswith("DGEMM_") and msg not in seen
+        seen.add(msg)
+    assert "unknown" in dg.dgemm_status_string(99)
+
+
+# Fake, never-dereferenced addresses: validation happens before any device call.
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+V = ctypes.c_void_p
+
+
+def call(fn, M, N, K, A, lda, B, ldb, C, ldc, out=0):
+    lib = dg.raw()
+    if fn == "gemm_f32":
+        return lib.gemm_f32(M, N, K, V(A), lda, V(B), ldb, V(C), ldc, None)
+    return getattr(lib, fn)(M, N, K, V(A), lda, V(B), ldb, V(C), ldc, out, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
+def test_validation_errors(fn):
+    es = 4 if fn == "gemm_f32" else 2
+    ok_ld = 64
+    assert call(fn, -1, 8, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, -1, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, 8, -1, PA, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, 8, 8, 0, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, 8, 8, PA, ok_ld, 0, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, 0, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
+    if fn != "gemm_f32":
+        assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld, out=2) == dg.DGEMM_ERR_INVALID_VALUE
+    assert call(fn, 8, 8, 72, PA, 64, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_LEADING_DIM
+    assert call(fn, 8, 72, 8, PA, ok_ld, PB, 64, PC, 80) == dg.DGEMM_ERR_LEADING_DIM
+    assert call(fn, 8, 72, 8, PA, ok_ld, PB, 80, PC, 64) == dg.DGEMM_ERR_LEADING_DIM
+    assert call(fn, 8, 8, 8, PA + 2, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_MISALIGNED
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB + 8, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_MISALIGNED
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, PC + 4, ok_ld) == dg.DGEMM_ERR_MISALIGNED
+    odd = 16 // es + 1  # a row pitch that is not a multiple of 16 bytes
+    assert call(fn, 8, 2, 2, PA, odd, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_MISALIGNED
+    assert call(fn, 8, 2, 2, PA, ok_ld, PB, odd, PC, ok_ld) == dg.DGEMM_ERR_MISALIGNED
+    # C overlapping A or B
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, PA + 64 * es, ok_ld) == dg.DGEMM_ERR_ALIAS
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, PB, ok_ld) == dg.DGEMM_ERR_ALIAS
+    # 32-bit descriptor range
+    huge = (1 << 31) // (256 * es)
+    assert call(fn, 8, 8, 8, PA, huge, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+    far = 0x7000000000
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // 128, far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
+def test_empty_output_is_a_no_op_without_device(fn):
+    # M == 0 or N == 0: nothing to write, no device needed, even with NULL pointers.
+    assert call(fn, 0, 8, 8, 0, 8, 0, 8, 0, 8) == dg.DGEMM_OK
+    assert call(fn, 8, 0, 8, 0, 8, 0, 1, 0, 1) == dg.DGEMM_OK
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (256, 256), (4096, 4096), (16384, 4096), (4000, 3000),
+                                 (257, 4097), (2560, 256), (256, 9000), (7777, 3333), (512, 512)])
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_tile_map_is_a_bijection(M, N, fmt):
+    info = dg.dgemm_tile_map(M, N, fmt)
+    tm_n = -(-M // info["tile_rows"])
+    tn_n = -(-N // info["tile_cols"])
+    assert info["num_wg"] == tm_n * tn_n
+    seen = set()
+    for wg in range(info["num_wg"]):
+        t = dg.dgemm_tile_map(M, N, fmt, wg)
+        assert 0 <= t["tile_m"] < tm_n and 0 <= t["tile_n"] < tn_n
+        seen.add((t["tile_m"], t["tile_n"]))
+    assert len(seen) == info["num_wg"]
+
+
+def test_tile_map_gives_each_xcd_a_compact_block():
+    """At 4096 x 4096 (16 x 16 tiles) the workgroups of one XCD (wg % 8) cover a
+    4 x 8 block of tiles: 4 A panels and 8 B panels instead of up to 32 each."""
+    for x in range(8):
+        tiles = [dg.dgemm_tile_map(4096, 4096, "bf16", wg) for wg in range(x, 256, 8)]
+        rows = {t["tile_m"] for t in tiles}
+        cols = {t["tile_n"] for t in tiles}
+        assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8
+
+
+def test_tile_map_rejects_bad_arguments():
+    lib = dg.raw()
+    z = ctypes.c_int()
+    assert lib.dgemm_tile_map(-1, 4, 1, 0, *[ctypes.byref(z)] * 5) == dg.DGEMM_ERR_INVALID_VALUE
+    assert lib.dgemm_tile_map(4, 4, 7, 0, *[ctypes.byref(z)] * 5) == dg.DGEMM_ERR_INVALID_VALUE

@@ -1,0 +1,186 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case draws seeded inputs, runs the library on cuda:0 and compares with
+the oracle on the same storage bytes: element by element within
+|C - C64| <= tol*S*(1+u) + u*|C64| (+ subnormal slack), bit for bit where the
+inputs make the answer exact.  C is prefilled with NaN and its row pitch gap
+must stay NaN, so missed and stray stores both show."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_matrix_amd as dg
+import oracle
+from oracle.parity import TOL_MFMA
+from synth_inputs import draw, pair, workload
+from tests.gpu_util import TORCH, dev_matrix, gap_untouched, round_pitch, sentinel_c, to64
+
+pytestmark = pytest.mark.gpu
+
+ENTRY = {"f32": dg.gemm_f32, "bf16": dg.gemm_bf16, "f16": dg.gemm_f16}
+COMBOS = [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")]
+
+
+def run(dtype, out, A, B, a_extra=0, b_extra=0, c_extra=4, stream=None):
+    M, K = A.shape
+    N = B.shape[1]
+    Ad = dev_matrix(A, dtype, round_pitch(K, dtype, a_extra))
+    Bd = dev_matrix(B, dtype, round_pitch(N, dtype, b_extra))
+    Cd = sentinel_c(M, N, out, round_pitch(N, out, c_extra))
+    ENTRY[dtype](Ad, Bd, Cd, stream=stream)
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return Cd
+
+
+def sample_rows(M, rng, extra=8):
+    cand = {0, 1, 31, 32, 127, 128, 255, 256, 257, M // 2, M - 257, M - 256, M - 255, M - 1}
+    cand |= set(int(r) for r in rng.integers(0, M, extra))
+    return np.array(sorted(r for r in cand if 0 <= r < M), dtype=np.int64)
+
+
+DIMS_MN = [1, 7, 33, 255, 256, 257]
+DIMS_K = [1, 7, 64, 65, 255, 257]
+
+
+@pytest.mark.parametrize("dtype,out", COMBOS)
+def test_small_and_ragged_shapes(dtype, out):
+    rng = np.random.default_rng(1000 + COMBOS.index((dtype, out)))
+    for M in DIMS_MN:
+        for N in DIMS_MN:
+            for K in DIMS_K:
+                print(f"case {dtype}->{out} {M}x{N}x{K}", flush=True)
+                A = draw(rng, (M, K), "normal", dtype)
+                B = draw(rng, (K, N), "normal", dtype)
+                C = run(dtype, out, A, B, a_extra=8, b_extra=8)
+                C64, S = oracle.gemm(dtype, A, B)
+                res = oracle.check(to64(C), C64, S, TOL_MFMA, out)
+                assert res["ok"], (M, N, K, res)
+                assert gap_untouched(C), (M, N, K)
+
+
+@pytest.mark.parametrize("dtype,out", COMBOS)
+@pytest.mark.parametrize("M,N,K", [(1000, 700, 1100), (512, 768, 4104), (300, 264, 200)])
+def test_exact_integer_inputs_bitwise(dtype, out, M, N, K):
+    """Integers in [-8, 8]: every partial sum is an integer below 2^24, so the fp32
+    accumulator is exact in any order; C must equal the oracle's C64 rounded once
+    to C's format, bit for bit.  This pins tiling, staging, the LDS layout, the
+    operand layouts, masking, the tile map and the epilogue."""
+    print(f"case int {dtype}->{out} {M}x{N}x{K}", flush=True)
+    A, B = pair(M, N, K, "ints", dtype, seed=2000 + M + N + K)
+    C = run(dtype, out, A, B, a_extra=8, b_extra=16)
+    C64, _ = oracle.gemm(dtype, A, B)
+    want = oracle.widen(out, oracle.round_to(out, C64))
+    assert np.array_equal(to64(C), want)
+    assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("name", ["f32_512", "f32_4096", "bf16_4096", "f16_4096",
+                                  "bf16_16384x4096x4096", "bf16_4000x3000x4104"])
+def test_workloads(name):
+    """The six workloads at full size; the oracle checks sampled rows (all rows
+    at 512^3), and no element of C may be left unwritten."""
+    A, B, meta = workload(name)
+    dtype, out, M = meta["dtype"], meta["out"], meta["M"]
+    print(f"case workload {name}", flush=True)
+    Ad = dev_matrix(A, dtype, A.shape[1])
+    Bd = dev_matrix(B, dtype, B.shape[1])
+    Cd = torch.full((M, meta["N"]), float("nan"), dtype=TORCH[out], device="cuda")
+    ENTRY[dtype](Ad, Bd, Cd)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(Cd.float()).any().item()), "unwritten elements"
+    rows = np.arange(M) if M <= 512 else sample_rows(M, np.random.default_rng(meta["seed"]))
+    C64, S = oracle.gemm(dtype, A, B, rows=rows)
+    got = to64(Cd[torch.from_numpy(rows).to("cuda")])
+    res = oracle.check(got, C64, S, TOL_MFMA, out, C_round=oracle.widen(out, oracle.round_to(out, C64)))
+    print(f"{name}: max err/bound {res['max_ratio']:.3g}, equal to the oracle's rounding "
+          f"{res['exact_frac']:.3f}", flush=True)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_exact_integer_full_size_freivalds(dtype):
+    """4096^3 with integer inputs and fp32 C: C is exact, so C.x == A.(B.x)
+    exactly in fp64 for integer vectors x (all values stay below 2^53).  Three
+    random x make a wrong element anywhere in C show with near certainty; rows
+    sampled against the oracle pin the values themselves."""
+    M = N = K = 4096
+    print(f"case freivalds {dtype}", flush=True)
+    A, B = pair(M, N, K, "ints", dtype, seed=3000)
+    C = run(dtype, "f32", A, B)
+    Cn = to64(C)
+    Aw = oracle.widen(dtype, A)
+    Bw = oracle.widen(dtype, B)
+    rng = np.random.default_rng(3001)
+    for _ in range(3):
+        x = rng.integers(-4, 5, N).astype(np.float64)
+        assert np.array_equal(Cn @ x, Aw @ (Bw @ x))
+        y = rng.integers(-4, 5, M).astype(np.float64)
+        assert np.array_equal(y @ Cn, (y @ Aw) @ Bw)
+    rows = sample_rows(M, rng)
+    C64, _ = oracle.gemm(dtype, A, B, rows=rows)
+    assert np.array_equal(Cn[rows], C64)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    A, B = pair(1024, 1024, 2048, "normal", "bf16", seed=4000)
+    C1 = run("bf16", "f32", A, B)
+    C2 = run("bf16", "f32", A, B)
+    assert torch.equal(C1, C2)
+
+
+def test_non_default_stream():
+    A, B = pair(520, 260, 300, "normal", "f16", seed=4100)
+    ref = run("f16", "f16", A, B)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run("f16", "f16", A, B, stream=s)
+    assert torch.equal(ref, got)
+
+
+@pytest.mark.parametrize("dtype,out", COMBOS)
+def test_leading_dimensions_larger_than_rows(dtype, out):
+    A, B = pair(333, 290, 515, "normal", dtype, seed=4200)
+    C = run(dtype, out, A, B, a_extra=136, b_extra=264, c_extra=72)
+    C64, S = oracle.gemm(dtype, A, B)
+    assert oracle.check(to64(C), C64, S, TOL_MFMA, out)["ok"]
+    assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("dtype,out", COMBOS)
+def test_k_zero_writes_zeros_and_empty_outputs(dtype, out):
+    A = np.zeros((300, 0), dtype=np.float32)
+    Ad = torch.zeros((300, 8), dtype=TORCH[dtype], device="cuda")[:, :0]
+    Bd = torch.zeros((1, 264), dtype=TORCH[dtype], device="cuda")[:0]
+    C = sentinel_c(300, 264, out)
+    ENTRY[dtype](Ad, Bd, C)
+    torch.cuda.synchronize()
+    assert bool((C.float() == 0).all().item()) and gap_untouched(C)
+    assert A.shape[1] == 0
+    C0 = torch.empty((0, 5), dtype=TORCH[out], device="cuda")
+    ENTRY[dtype](torch.zeros((0, 3), dtype=TORCH[dtype], device="cuda"),
+                 torch.zeros((3, 5), dtype=TORCH[dtype], device="cuda"), C0)
+
+
+def test_invalid_arguments_leave_c_untouched():
+    A, B = pair(64, 64, 64, "normal", "bf16", seed=4300)
+    Ad = dev_matrix(A, "bf16")
+    Bd = dev_matrix(B, "bf16")
+    C = sentinel_c(64, 64, "f32")
+    raw = torch.full((64 * 72 + 8,), 0, dtype=torch.bfloat16, device="cuda")
+    mis = raw[1:1 + 64 * 72].view(64, 72)[:, :64]   # base misaligned by 2 bytes
+    with pytest.raises(dg.DgemmError) as e:
+        dg.gemm_bf16(mis, Bd, C)
+    assert e.value.status == dg.DGEMM_ERR_MISALIGNED
+    Cal = torch.full((64, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dg.DgemmError) as e:
+        dg.gemm_bf16(Cal, Bd, Cal)
+    assert e.value.status == dg.DGEMM_ERR_ALIAS
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(C).all().item())
+    assert bool(torch.isnan(Cal.float()).all().item())
+    dg.gemm_bf16(Ad, Bd, C)
+    torch.cuda.synchronize()
+    C64, S = oracle.gemm("bf16", A, B)
+    assert oracle.check(to64(C), C64, S, TOL_MFMA, "f32")["ok"]
