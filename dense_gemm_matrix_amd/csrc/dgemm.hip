@@ -103,9 +103,22 @@ __device__ __forceinline__ int lds_index(int row, int chunk) {
     return row * ROW_CHUNKS + (chunk ^ ((row ^ (row >> 3)) & 7));
 }
 
+// A raw buffer resource covering [base, base + bytes), the range rounded up to
+// 16 bytes.  The buffer unit range-checks whole dwords, so a range ending in
+// the middle of a dword (an odd count of 16-bit elements) would return the
+// last element as zero.  Rounding up is safe: bases and row pitches are 16-byte
+// aligned, so the extra bytes share a 16-byte chunk (hence a page) with the
+// last element; they are masked (A's K tail) or feed only unstored outputs
+// (B's columns past N).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, (int)BUF_WORD3);
+    const int64_t rounded = (bytes + 15) & ~(int64_t)15;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)rounded, (int)BUF_WORD3);
 }
+
+// Reinterpret a 32-bit word as fp32.  The word is taken by value: clang's
+// __builtin_bit_cast applied directly to an ext-vector element subscript
+// (v[e]) reads element 0 whatever e is, so callers pass v[e] through here.
+__device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
@@ -275,8 +288,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                __builtin_bit_cast(float, a[mi][e]),
-                                __builtin_bit_cast(float, b[nj][e]), acc[mi][nj], 0, 0, 0);
+                                as_float(a[mi][e]), as_float(b[nj][e]), acc[mi][nj], 0, 0, 0);
                     }
                 }
             }
