@@ -1,47 +1,48 @@
 // dgemm.hip -- dense GEMM C = A*B for gfx950 (MI355X), behind the C ABI of
 // include/dgemm.h.
 //
-// One kernel template serves fp32, bf16 and fp16 inputs.  Per workgroup:
+// Two kernels share the tile map, the 256 x 256 macro-tile, the wave layout
+// and the epilogue:
 //
-//   * a 256 x 256 output macro-tile, 256 threads = 4 waves of 64 lanes in a
-//     2 x 2 layout, each wave owning a 128 x 128 sub-tile held as 4 x 4
-//     v_mfma 32x32 accumulator blocks (256 fp32 accumulators per lane, kept in
-//     registers for the whole K loop);
-//   * per K step, a 256 x 128-byte slab of A and of B staged in LDS (BK = 64
-//     elements for 16-bit inputs, 32 for fp32), double buffered: the next
-//     step's global loads are in flight while the current step computes, and
-//     one barrier per step separates the LDS write of step k+1 from the reads
-//     of step k;
-//   * A is staged as it lies in memory (K-contiguous rows).  B is row-major
-//     (N-contiguous), but a matrix instruction wants each lane's operand to run
-//     along K, so each thread loads an 8-row block of B and transposes it in
-//     registers before writing it to LDS as K-contiguous rows;
-//   * LDS rows are 8 chunks of 16 bytes; chunk c of row r is stored at slot
-//     c ^ phi(r).  Only chunk bits are permuted, so every 16-byte access stays
-//     aligned (the principle of the sgemm tf32 page's section 3 swizzles and
-//     the hgemm page's section 2), and phi is chosen for the access patterns
-//     used here: the matrix-operand reads (8 lanes on 8 consecutive rows, same
-//     chunk) and both staging writes (8 lanes on 8 chunks of one row);
-//   * a bijective workgroup -> tile map that keeps each XCD's workgroups on a
-//     compact block of tiles (the sgemm tf32 page's section 4 Grid Swizzling,
-//     adapted to 8 XCDs with private L2s);
-//   * buffer loads with per-step resource descriptors: rows past M (A) and K
-//     (B) fall outside the descriptor's range and read as zero, the K tail of
-//     A is masked to exact zeros, and the epilogue stores only inside M x N.
-//     No host padding (the nine-levels tutorial's section 2.9 and 6.1 offer
-//     padding or predication; predication is chosen).
+//   * gemm16_kernel (bf16 / fp16 inputs).  Both operands go global -> LDS with
+//     direct-to-LDS buffer loads (no VGPR staging, no LDS write instructions)
+//     into a 4-stage ring of BK = 32 slabs, issued about three steps ahead of
+//     their use.  A is stored K-contiguous and read with ds_read_b128.  B is
+//     stored as it lies in memory (row-major, N-contiguous) and read with
+//     ds_read_b64_tr_b16: within each 16-lane group that instruction performs
+//     a 4 x 4 transpose of 4-element row pieces, which hands every lane the
+//     four consecutive k of one column that the matrix instruction's B operand
+//     needs.  v_mfma_f32_32x32x16_{bf16,f16}.
+//   * gemm_kernel (fp32 inputs).  gfx950 has no xf32 matrix instruction, so
+//     products use full-precision v_mfma_f32_32x32x2_f32.  Operands are staged
+//     through registers (B's 8 x 4 fp32 blocks are transposed by register
+//     renaming), double-buffered in LDS with BK = 32.
 //
-// gfx950 has no xf32 matrix instruction, so fp32 inputs use full-precision
-// v_mfma_f32_32x32x2_f32.  Matrix instructions' internal k order is not
-// observable through the ABI: a lane group's operand chunk carries the same k
-// indices for A and for B, so any permutation of k inside an instruction
-// cancels.
+// Shared structure, per workgroup: 256 threads = 4 waves of 64 lanes in a
+// 2 x 2 layout, each wave owning a 128 x 128 sub-tile held as 4 x 4 blocks of
+// 32 x 32 accumulators (256 fp32 per lane, register-resident for the whole K
+// loop).  LDS rows are split into 16-byte chunks whose positions are XORed
+// with a function of the row, so every 16-byte access stays aligned (the
+// principle of the sgemm tf32 page's section 3 swizzles and the hgemm page's
+// section 2) while the access patterns used here hit distinct LDS banks.  A
+// bijective workgroup -> tile map keeps each XCD's workgroups on a compact
+// block of tiles (the sgemm tf32 page's section 4 Grid Swizzling, adapted to 8
+// XCDs with private L2s).  Buffer loads use per-step resource descriptors:
+// rows past M (A) and past K (B) fall outside the range and read as zero, A's
+// K tail is forced to exact zeros, and the epilogue stores only inside M x N;
+// no host padding (the nine-levels tutorial's sections 2.9 and 6.1 offer
+// padding or predication; predication is chosen).
+//
+// Matrix instructions' internal k order is not observable through the ABI: a
+// lane group's operand carries the same k indices for A and for B, so any
+// permutation of k inside an instruction cancels.
 
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "dgemm.h"
 
@@ -51,6 +52,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 enum InFmt { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
 enum OutFmt { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
@@ -58,21 +62,16 @@ enum OutFmt { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 constexpr int BM = 256;                       // macro-tile rows
 constexpr int BN = 256;                       // macro-tile columns
 constexpr int NTHREADS = 256;                 // 4 waves
-constexpr int ROW_CHUNKS = 8;                 // 16-byte chunks per staged row (128 bytes of K)
-constexpr int STAGE_CHUNKS = BM * ROW_CHUNKS; // one operand's stage: 2048 chunks = 32 KiB
 constexpr int GROUP_M = 4;                    // tile rows per strip in the tile walk
 constexpr int NUM_XCD = 8;                    // XCDs that workgroups are dealt across
 constexpr uint32_t BUF_WORD3 = 0x00020000u;   // raw buffer: 32-bit data format, no swizzle
+constexpr uint32_t OOB = 0x7ffffff0u;         // a buffer offset past any range: reads zero
 constexpr int64_t DESC_LIMIT = (int64_t)1 << 31;
 
-template <int IN> struct InTraits;
-template <> struct InTraits<IN_F32> { static constexpr int esize = 4, epc = 4, bk = 32; };
-template <> struct InTraits<IN_BF16> { static constexpr int esize = 2, epc = 8, bk = 64; };
-template <> struct InTraits<IN_F16> { static constexpr int esize = 2, epc = 8, bk = 64; };
-// epc = elements per 16-byte chunk; bk = elements of K per step = ROW_CHUNKS * epc.
+// K per step: 32 for both kernels (fp32: 128-byte LDS rows; 16-bit: 64-byte rows).
+constexpr int BK = 32;
 
 int in_esize(int in) { return in == IN_F32 ? 4 : 2; }
-int in_bk(int in) { return in == IN_F32 ? 32 : 64; }
 
 // Workgroup -> output tile.  Step 1: workgroups are dealt to XCDs in turn, so
 // wg % 8 is its XCD; give XCD x the contiguous run of tile indices
@@ -96,23 +95,20 @@ __host__ __device__ inline void map_tile(int wg, int tiles_m, int tiles_n, int& 
     tn = rem / rows_in_strip;
 }
 
-// LDS slot of chunk c in staged row r.  With phi(r) = (r ^ (r >> 3)) & 7, the 8
-// consecutive rows an operand read touches get 8 distinct slots, and so do the
-// 8 aligned rows of any 16-row group with equal parity.
-__device__ __forceinline__ int lds_index(int row, int chunk) {
-    return row * ROW_CHUNKS + (chunk ^ ((row ^ (row >> 3)) & 7));
-}
-
 // A raw buffer resource covering [base, base + bytes), the range rounded up to
 // 16 bytes.  The buffer unit range-checks whole dwords, so a range ending in
 // the middle of a dword (an odd count of 16-bit elements) would return the
 // last element as zero.  Rounding up is safe: bases and row pitches are 16-byte
 // aligned, so the extra bytes share a 16-byte chunk (hence a page) with the
 // last element; they are masked (A's K tail) or feed only unstored outputs
-// (B's columns past N).
+// (B's columns past N).  bytes <= 0 gives an empty range.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
-    const int64_t rounded = (bytes + 15) & ~(int64_t)15;
+    const int64_t rounded = bytes > 0 ? (bytes + 15) & ~(int64_t)15 : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)rounded, (int)BUF_WORD3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
 }
 
 // Reinterpret a 32-bit word as fp32.  The word is taken by value: clang's
@@ -120,27 +116,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
 // (v[e]) reads element 0 whatever e is, so callers pass v[e] through here.
 __device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int voffset) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Zero the elements of a chunk at and after `valid` (valid <= 0: all of them).
-template <int EPC>
-__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid) {
-    u32x4 out;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint32_t w = v[d];
-        if (EPC == 4) {
-            w = (d < valid) ? w : 0u;
-        } else {
-            const uint32_t lo = (2 * d < valid) ? 0x0000ffffu : 0u;
-            const uint32_t hi = (2 * d + 1 < valid) ? 0xffff0000u : 0u;
-            w &= (lo | hi);
-        }
-        out[d] = w;
-    }
-    return out;
+// One direct-to-LDS 16-byte-per-lane buffer load: lane l's 16 bytes from
+// rsrc + voffset land at LDS byte lds + 16 l.  Issued as inline assembly so that
+// the compiler does not guard every later LDS read with a wait for ALL such
+// loads (it cannot tell which LDS bytes they write); the kernel waits for them
+// explicitly with s_waitcnt vmcnt before the barrier that publishes a stage.
+// M0 is reserved to the compiler, which warns about the clobber; nothing else
+// in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate: wait until at most vm vector-memory and lgkm LDS/scalar
+// operations of this wave are outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 0xf) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xf) << 8);
 }
 
 template <int OUT>
@@ -154,17 +155,249 @@ __device__ __forceinline__ void store_c(char* C, int64_t idx, float v) {
     }
 }
 
+// Epilogue shared by both kernels.  32x32 accumulator layout: lane (g, li)
+// holds column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4.
+template <int OUT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], char* C, int M, int N,
+                                           int ldc, int row0, int col0, int g, int li) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) {
+            const int col = col0 + nj * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (row < M && col < N) store_c<OUT>(C, (int64_t)row * ldc + col, acc[mi][nj][r]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 16-bit kernel
+
+constexpr int S16 = 4;                         // LDS stages
+constexpr int A16_ROW = BK * 2;                // 64 bytes: 4 chunks of 8 elements
+constexpr int A16_STAGE = BM * A16_ROW;        // 16 KiB
+constexpr int B16_ROW = BN * 2;                // 512 bytes: 32 chunks
+constexpr int B16_STAGE = BK * B16_ROW;        // 16 KiB
+constexpr int LOADS16 = 8;                     // direct-to-LDS loads per thread per stage
+
+// Byte offset of chunk c (0..3) of A row r in a stage.  The XOR spreads the 8
+// (or 16) consecutive rows one operand read touches over distinct bank groups.
+__device__ __forceinline__ int a16_off(int row, int chunk) {
+    return row * A16_ROW + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+}
+// Byte offset of chunk c (0..31) of B row k in a stage.  The transpose read of
+// one 16-lane group touches 4 consecutive k rows x 32 bytes (two groups: x 64
+// bytes); the XOR puts the rows' pieces in distinct bank groups.
+__device__ __forceinline__ int b16_swz(int k) { return ((k & 3) << 1) ^ ((k & 1) << 3); }
+__device__ __forceinline__ int b16_off(int k, int chunk) {
+    return k * B16_ROW + ((chunk ^ b16_swz(k)) << 4);
+}
+
 template <int IN, int OUT>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(
+__global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n) {
-    using T = InTraits<IN>;
-    constexpr int ES = T::esize;
-    constexpr int EPC = T::epc;
-    constexpr int BK = T::bk;
+    __shared__ __attribute__((aligned(1024))) char smem[S16 * (A16_STAGE + B16_STAGE)];
+    char* const smA = smem;
+    char* const smB = smem + S16 * A16_STAGE;
 
-    // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x 32 KiB.
-    __shared__ u32x4 lds[2][2][STAGE_CHUNKS];
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int nk = (K + BK - 1) / BK;
+
+    // Each direct-to-LDS instruction fills a 1 KiB block lane-linearly (lane l
+    // -> bytes 16 l .. 16 l + 15), so the swizzle is applied on the global side:
+    // lane l fetches the chunk that belongs in its slot.  Wave w fills blocks
+    // 4 w .. 4 w + 3 of each operand's stage: A rows 16 b .. 16 b + 15 (4 chunks
+    // each), B k-rows 2 b, 2 b + 1 (32 chunks each).
+    int voffA[4], kchA[4], voffB[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int blk = wave * 4 + j;
+        const int rowA = blk * 16 + (lane >> 2);
+        const int cA = (lane & 3) ^ (((rowA >> 1) ^ (rowA >> 3)) & 3);
+        voffA[j] = rowA * lda * 2 + cA * 16;
+        kchA[j] = cA * 8;
+        const int kB = blk * 2 + (lane >> 5);
+        const int cB = (lane & 31) ^ b16_swz(kB);
+        voffB[j] = kB * ldb * 2 + cB * 16;
+    }
+
+    // Global loads of step kt into LDS stage kt % S16.  Steps past the end get
+    // empty ranges (they only keep the per-step load count uniform).
+    auto issue_stage = [&](int kt) {
+        const int s = kt % S16;
+        const int k0 = kt * BK;
+        const int krem = K - k0;
+        const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
+        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 2 : 0;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
+        const int rows_b = krem < BK ? krem : BK;
+        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 2;
+        const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 2 : 0;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // A chunks wholly past K read as zero (a straddling chunk is fixed in LDS).
+            const int off = (kchA[j] < krem) ? voffA[j] : (int)OOB;
+            dma16(rsa, lds_addr(smA + s * A16_STAGE + (wave * 4 + j) * 1024), off);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dma16(rsb, lds_addr(smB + s * B16_STAGE + (wave * 4 + j) * 1024), voffB[j]);
+    };
+
+    // When K is not a multiple of 8, the last stage's A chunk that straddles K
+    // holds other data past K (row padding or the next row); zero it in LDS, so
+    // that 0 * (NaN or Inf) can never reach the sum.
+    auto fix_tail = [&]() {
+        const int kt = nk - 1;
+        const int s = kt % S16;
+        const int kin = K - kt * BK;         // valid k in the last stage, 1..31
+        const int chunk = kin >> 3;          // the straddling chunk
+        const int first = kin & 7;           // first invalid element in it
+        short* p = (short*)(smA + s * A16_STAGE + a16_off(tid, chunk));
+        for (int e = first; e < 8; ++e) p[e] = 0;
+    };
+
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int g = lane >> 5;          // lane group: k half of a 16-k chunk pair
+    const int li = lane & 31;         // row of A within a 32-row block
+    const int ta = (lane >> 2) & 3;   // transpose read: source k row within the group
+    const int tq = lane & 3;          // transpose read: source 4-column piece
+    const int tg = (lane >> 4) & 1;   // transpose read: the 16-lane group's column half
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    // Operand fragments of one 16-k chunk pair: A as 4 x 8 consecutive k of a
+    // row; B as 4 x (two transpose reads of 4 consecutive k of a column).  Two
+    // sets alternate so one pair's reads overlap the other pair's MFMAs.
+    u32x4 fa[2][4];
+    s16x4 fb[2][4][2];
+
+    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
+        const int s = kt % S16;
+        const char* sa = smA + s * A16_STAGE;
+        const char* sb = smB + s * B16_STAGE;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            a[mi] = *(const u32x4*)(sa + a16_off(wm * 128 + mi * 32 + li, 2 * kp + g));
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = kp * 16 + 8 * g + 4 * h + ta;
+                const int c = wn * 16 + nj * 4 + 2 * tg + (tq >> 1);
+                b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t*)(sb + b16_off(k, c) + (tq & 1) * 8));
+            }
+        }
+    };
+
+    auto mfma_frags = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj) {
+                const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                if constexpr (IN == IN_BF16) {
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, bv),
+                        acc[mi][nj], 0, 0, 0);
+                } else {
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv),
+                        acc[mi][nj], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Wait until at most VM of this wave's direct-to-LDS loads are in flight and
+    // its LDS accesses are done, then barrier.
+    auto sync = [&](auto vm_tag) {
+        constexpr int VM = decltype(vm_tag)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using OneStepLeft = std::integral_constant<int, (S16 - 1) * LOADS16>;
+    using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * LOADS16>;
+
+    // Schedule.  Prologue: loads of steps 0..3.  Step kt: read the fragments
+    // of pair 1 while pair 0's MFMAs run; wait for step kt + 1's loads (steps
+    // kt + 2, kt + 3 may still be in flight) and barrier, which also retires
+    // every wave's reads of stage kt % 4; refill that stage with step kt + 4;
+    // read pair 0 of step kt + 1 while pair 1's MFMAs of step kt run.
+    if (nk > 0) {
+#pragma unroll
+        for (int s = 0; s < S16; ++s) issue_stage(s);
+        sync(OneStepLeft{});
+        if ((K & 7) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            read_frags(kt, 1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            sync(TwoStepsLeft{});
+            if ((K & 7) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
+            issue_stage(kt + S16);
+            if (kt + 1 < nk) read_frags(kt + 1, 0, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // No direct-to-LDS write may still be in flight when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+    store_tile<OUT>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li);
+}
+
+// ---------------------------------------------------------------- fp32 kernel
+
+constexpr int ROW_CHUNKS32 = 8;                  // 16-byte chunks per staged row (32 fp32)
+constexpr int STAGE_CHUNKS32 = BM * ROW_CHUNKS32;  // one operand's stage: 32 KiB
+
+// LDS slot of chunk c in staged row r.  With phi(r) = (r ^ (r >> 3)) & 7, the 8
+// consecutive rows an operand read touches get 8 distinct slots, and so do the
+// 8 aligned rows of any 16-row group with equal parity.
+__device__ __forceinline__ int lds32_index(int row, int chunk) {
+    return row * ROW_CHUNKS32 + (chunk ^ ((row ^ (row >> 3)) & 7));
+}
+
+// Zero the fp32 elements of a chunk at and after `valid` (valid <= 0: all).
+__device__ __forceinline__ u32x4 mask_tail32(u32x4 v, int valid) {
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = (d < valid) ? (uint32_t)v[d] : 0u;
+    return out;
+}
+
+__global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n) {
+    // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x 32 KiB.  Both operands are
+    // stored K-contiguous: B is transposed on its way through registers.
+    __shared__ u32x4 lds[2][2][STAGE_CHUNKS32];
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -181,28 +414,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(
     // A staging: thread -> chunk ac of rows ar0 + 32 i, i = 0..7.
     const int ac = tid & 7;
     const int ar0 = tid >> 3;
-    // B staging: thread -> a block of 8 K-rows (kb) by one 16-byte column chunk (nb).
-    constexpr int KB_COUNT = BK / 8;  // 8 (16-bit) or 4 (fp32)
-    const int kb = tid % KB_COUNT;
-    const int nb = tid / KB_COUNT;
+    // B staging: thread -> a block of 8 K-rows (kb) by 4 columns (nb).
+    const int kb = tid & 3;
+    const int nb = tid >> 2;
 
     int voff_a[8], voff_b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        voff_a[i] = (ar0 + 32 * i) * lda * ES + ac * 16;
-        voff_b[i] = (kb * 8 + i) * ldb * ES + nb * 16;
+        voff_a[i] = (ar0 + 32 * i) * lda * 4 + ac * 16;
+        voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
     }
 
     u32x4 ra[8], rb[8];
 
     auto load_step = [&](int kt, bool tail) {
         const int k0 = kt * BK;
-        const char* abase = A + ((int64_t)m0 * lda + k0) * ES;
-        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * ES;
+        const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
+        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
         const int rows_b = (K - k0) < BK ? (K - k0) : BK;
-        const char* bbase = B + ((int64_t)k0 * ldb + n0) * ES;
-        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * ES;
+        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
+        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
 #pragma unroll
         for (int i = 0; i < 8; ++i) ra[i] = load16(rsa, voff_a[i]);
@@ -211,41 +443,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(
         if (tail) {
             // Columns of A at or past K hold other data (row padding or the next
             // row); they must be exact zeros, since the matching B rows are.
-            const int valid = K - k0 - ac * EPC;
+            const int valid = K - k0 - ac * 4;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ra[i] = mask_tail<EPC>(ra[i], valid);
+            for (int i = 0; i < 8; ++i) ra[i] = mask_tail32(ra[i], valid);
         }
     };
 
     auto store_step = [&](int s) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds[s][0][lds_index(ar0 + 32 * i, ac)] = ra[i];
-        if (EPC == 8) {
-            // 8 K-rows x 8 columns of 16-bit values -> 8 columns x 8 K values.
+        for (int i = 0; i < 8; ++i) lds[s][0][lds32_index(ar0 + 32 * i, ac)] = ra[i];
+        // 8 K-rows x 4 columns -> 4 columns x two chunks of 4 K values.
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int d = cc >> 1;
+        for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
                 u32x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t x = rb[2 * e][d];
-                    const uint32_t y = rb[2 * e + 1][d];
-                    v[e] = (cc & 1) ? ((x >> 16) | (y & 0xffff0000u))
-                                    : ((x & 0x0000ffffu) | (y << 16));
-                }
-                lds[s][1][lds_index(nb * 8 + cc, kb)] = v;
-            }
-        } else {
-            // 8 K-rows x 4 fp32 columns -> 4 columns x two chunks of 4 K values.
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
-                    lds[s][1][lds_index(nb * 4 + cc, kb * 2 + h)] = v;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
+                lds[s][1][lds32_index(nb * 4 + cc, kb * 2 + h)] = v;
             }
         }
     };
@@ -263,66 +478,67 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
-    auto compute_step = [&](int s) {
+    // Operand fragments for one chunk pair (8 k): lane group g reads chunk
+    // 2 * kp + g of its 4 A rows and 4 B columns.  Two register sets alternate
+    // so that the reads for pair kp + 1 are in flight while kp computes.
+    u32x4 fa[2][4], fb[2][4];
+
+    auto read_frags = [&](int s, int kp, u32x4 (&a)[4], u32x4 (&b)[4]) {
+        const int ch = 2 * kp + g;
 #pragma unroll
-        for (int kp = 0; kp < ROW_CHUNKS / 2; ++kp) {
-            const int ch = 2 * kp + g;
-            u32x4 a[4], b[4];
+        for (int mi = 0; mi < 4; ++mi) a[mi] = lds[s][0][lds32_index(wm * 128 + mi * 32 + li, ch)];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) a[mi] = lds[s][0][lds_index(wm * 128 + mi * 32 + li, ch)];
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj) b[nj] = lds[s][1][lds_index(wn * 128 + nj * 32 + li, ch)];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-                for (int nj = 0; nj < 4; ++nj) {
-                    if (IN == IN_BF16) {
-                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, b[nj]),
-                            acc[mi][nj], 0, 0, 0);
-                    } else if (IN == IN_F16) {
-                        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, b[nj]),
-                            acc[mi][nj], 0, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                as_float(a[mi][e]), as_float(b[nj][e]), acc[mi][nj], 0, 0, 0);
-                    }
-                }
-            }
-        }
+        for (int nj = 0; nj < 4; ++nj) b[nj] = lds[s][1][lds32_index(wn * 128 + nj * 32 + li, ch)];
     };
 
+    auto mfma_frags = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        as_float(a[mi][e]), as_float(b[nj][e]), acc[mi][nj], 0, 0, 0);
+    };
+
+    // Schedule of one K step (stage `cur` in LDS, stage cur ^ 1 being filled):
+    // global loads for step kt + 1 -> registers; pairs 0, 1, 2: read the next
+    // pair's fragments, then compute; registers -> LDS stage cur ^ 1; barrier;
+    // read pair 0 of stage cur ^ 1, then compute pair 3 (already in registers),
+    // which covers that read's latency.  sched_barrier keeps the compiler from
+    // sinking the fragment reads down to their uses.
     if (nk > 0) {
         load_step(0, ragged_k && nk == 1);
         store_step(0);
         __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             const bool more = kt + 1 < nk;
             if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
-            compute_step(cur);
+            read_frags(cur, 1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 2, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 3, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
             if (more) store_step(cur ^ 1);
             __syncthreads();
+            if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // Epilogue.  32x32 accumulator layout: lane (g, li) holds column li and,
-    // in register r, row 8 * (r / 4) + 4 * g + r % 4.
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-            const int col = n0 + wn * 128 + nj * 32 + li;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (row < M && col < N) store_c<OUT>(C, (int64_t)row * ldc + col, acc[mi][nj][r]);
-            }
-        }
-    }
+    store_tile<OUT_F32>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li);
 }
 
 // ---------------------------------------------------------------- host side
@@ -372,7 +588,7 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
     }
     // Buffer descriptors address one 256-row panel of A and one K step of B
     // with 32-bit offsets.
-    if ((int64_t)BM * lda * es >= DESC_LIMIT || (int64_t)in_bk(in) * ldb * es >= DESC_LIMIT)
+    if ((int64_t)BM * lda * es >= DESC_LIMIT || (int64_t)BK * ldb * es >= DESC_LIMIT)
         return DGEMM_ERR_TOO_LARGE;
     const int64_t tiles = ((int64_t)(M + BM - 1) / BM) * ((int64_t)(N + BN - 1) / BN);
     if (tiles > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
@@ -389,7 +605,12 @@ int launch(int M, int N, int K, const void* A, int lda, const void* B, int ldb, 
     const char* b = (const char*)B;
     char* c = (char*)C;
     void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n};
-    hipError_t e = hipLaunchKernel((const void*)gemm_kernel<IN, OUT>, dim3((unsigned)ntiles),
+    const void* fn;
+    if constexpr (IN == IN_F32)
+        fn = (const void*)gemm32_kernel;
+    else
+        fn = (const void*)gemm16_kernel<IN, OUT>;
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)ntiles),
                                    dim3(NTHREADS), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? DGEMM_OK : DGEMM_ERR_LAUNCH;
 }
@@ -406,8 +627,10 @@ int gemm_entry(int M, int N, int K, const void* A, int lda, const void* B, int l
     st = check_device();
     if (st != DGEMM_OK) return st;
     if (out == DGEMM_OUT_F32) return launch<IN, OUT_F32>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
-    if (IN == IN_BF16) return launch<IN_BF16, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
-    return launch<IN_F16, OUT_F16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
+    if constexpr (IN == IN_BF16)
+        return launch<IN_BF16, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
+    else
+        return launch<IN_F16, OUT_F16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
 }
 
 }  // namespace

@@ -49,7 +49,7 @@ typedef enum {
     DGEMM_ERR_LEADING_DIM = 2,   /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N)           */
     DGEMM_ERR_MISALIGNED = 3,    /* a base pointer or a row pitch in bytes not a multiple of 16   */
     DGEMM_ERR_ALIAS = 4,         /* C's byte range overlaps A's or B's                           */
-    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 128*ldb bytes reach 2 GiB (32-bit offsets)  */
+    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 32*ldb*esize bytes reach 2 GiB (32-bit offsets) */
     DGEMM_ERR_DEVICE = 6,        /* no current device, or it is not a gfx950                     */
     DGEMM_ERR_LAUNCH = 7         /* the kernel launch reported an error                          */
 } dgemm_status;

@@ -85,7 +85,8 @@ def test_validation_errors(fn):
     huge = (1 << 31) // (256 * es)
     assert call(fn, 8, 8, 8, PA, huge, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
     far = 0x7000000000
-    assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // 128, far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // (32 * es), far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+
 
 
 @pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
