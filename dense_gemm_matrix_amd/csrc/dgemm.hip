@@ -6,8 +6,9 @@
 //
 //   * gemm16_kernel (bf16 / fp16 inputs).  Both operands go global -> LDS with
 //     direct-to-LDS buffer loads (no VGPR staging, no LDS write instructions)
-//     into a 4-stage ring of BK = 32 slabs, issued about three steps ahead of
-//     their use.  A is stored K-contiguous and read with ds_read_b128.  B is
+//     into a ring of S16 stages of BK16-deep slabs (2 x 64 at present: of the
+//     settings that fit 160 KiB, measured fastest; 4 x 32 and 5 x 32 were
+//     slower), each issued one step before its use.  A is stored K-contiguous and read with ds_read_b128.  B is
 //     stored as it lies in memory (row-major, N-contiguous) and read with
 //     ds_read_b64_tr_b16: within each 16-lane group that instruction performs
 //     a 4 x 4 transpose of 4-element row pieces, which hands every lane the
@@ -126,12 +127,15 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // the compiler does not guard every later LDS read with a wait for ALL such
 // loads (it cannot tell which LDS bytes they write); the kernel waits for them
 // explicitly with s_waitcnt vmcnt before the barrier that publishes a stage.
+// An LDS DMA needs one wait state after the SALU write of M0 that it reads
+// (the compiler keeps one instruction between them for its own LDS DMA), hence
+// the s_nop.
 // M0 is reserved to the compiler, which warns about the clobber; nothing else
 // in these kernels uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds), "v"(voffset), "s"(rsrc)
                  : "memory", "m0");
@@ -176,21 +180,33 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], char* C, i
 
 // ---------------------------------------------------------------- 16-bit kernel
 
-constexpr int S16 = 4;                         // LDS stages
-constexpr int A16_ROW = BK * 2;                // 64 bytes: 4 chunks of 8 elements
-constexpr int A16_STAGE = BM * A16_ROW;        // 16 KiB
+constexpr int BK16 = 64;                       // K per stage
+constexpr int S16 = 2;                         // LDS stages
+constexpr int KP16 = BK16 / 16;                // 16-k chunk pairs per stage
+constexpr int A16_CH = BK16 / 8;               // 16-byte chunks per A row
+constexpr int A16_ROW = BK16 * 2;              // bytes per staged A row
+constexpr int A16_STAGE = BM * A16_ROW;        // bytes per A stage
 constexpr int B16_ROW = BN * 2;                // 512 bytes: 32 chunks
-constexpr int B16_STAGE = BK * B16_ROW;        // 16 KiB
-constexpr int LOADS16 = 8;                     // direct-to-LDS loads per thread per stage
+constexpr int B16_STAGE = BK16 * B16_ROW;      // bytes per B stage
+constexpr int A16_DMA = A16_STAGE / 1024 / 4;  // direct-to-LDS loads per wave per stage (A)
+constexpr int B16_DMA = B16_STAGE / 1024 / 4;  // ... (B)
+constexpr int LOADS16 = A16_DMA + B16_DMA;     // per thread per stage
+constexpr int A16_RPB = 1024 / A16_ROW;        // A rows per 1 KiB load block
+static_assert(S16 * (A16_STAGE + B16_STAGE) <= 160 * 1024, "LDS budget");
+static_assert((S16 - 1) * LOADS16 <= 63, "vmcnt range");
 
-// Byte offset of chunk c (0..3) of A row r in a stage.  The XOR spreads the 8
-// (or 16) consecutive rows one operand read touches over distinct bank groups.
+// Byte offset of chunk c (0..3) of A row r in a stage.  ds_read_b128 serves
+// groups of 4 consecutive lanes from a 64-byte window of banks (measured on
+// gfx950 with SQ_LDS_BANK_CONFLICT), and the 4 lanes of a group read 4
+// consecutive rows at one chunk: a16_phi gives those rows 4 distinct slots.
+__device__ __forceinline__ int a16_phi(int row) { return (row ^ (row >> 2)) & (A16_CH - 1); }
 __device__ __forceinline__ int a16_off(int row, int chunk) {
-    return row * A16_ROW + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+    return row * A16_ROW + ((chunk ^ a16_phi(row)) << 4);
 }
-// Byte offset of chunk c (0..31) of B row k in a stage.  The transpose read of
-// one 16-lane group touches 4 consecutive k rows x 32 bytes (two groups: x 64
-// bytes); the XOR puts the rows' pieces in distinct bank groups.
+// Byte offset of chunk c (0..31) of B row k in a stage.  ds_read_b64_tr_b16
+// serves 32 lanes from a 256-byte window (measured), and those 32 lanes read 4
+// consecutive k rows x 64 bytes; the XOR puts the four rows' pieces in
+// distinct quarters of the window.
 __device__ __forceinline__ int b16_swz(int k) { return ((k & 3) << 1) ^ ((k & 1) << 3); }
 __device__ __forceinline__ int b16_off(int k, int chunk) {
     return k * B16_ROW + ((chunk ^ b16_swz(k)) << 4);
@@ -213,22 +229,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     const int n0 = tn * BN;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int cols_b = (N - n0) < BN ? (N - n0) : BN;
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K + BK16 - 1) / BK16;
 
     // Each direct-to-LDS instruction fills a 1 KiB block lane-linearly (lane l
     // -> bytes 16 l .. 16 l + 15), so the swizzle is applied on the global side:
-    // lane l fetches the chunk that belongs in its slot.  Wave w fills blocks
-    // 4 w .. 4 w + 3 of each operand's stage: A rows 16 b .. 16 b + 15 (4 chunks
-    // each), B k-rows 2 b, 2 b + 1 (32 chunks each).
-    int voffA[4], kchA[4], voffB[4];
+    // lane l fetches the chunk that belongs in its slot.  Wave w fills the
+    // blocks w * DMA .. (w + 1) * DMA - 1 of each operand's stage: for A,
+    // A16_RPB rows of A16_CH chunks each; for B, 2 k-rows of 32 chunks each.
+    int voffA[A16_DMA], kchA[A16_DMA], voffB[B16_DMA];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int blk = wave * 4 + j;
-        const int rowA = blk * 16 + (lane >> 2);
-        const int cA = (lane & 3) ^ (((rowA >> 1) ^ (rowA >> 3)) & 3);
+    for (int j = 0; j < A16_DMA; ++j) {
+        const int rowA = (wave * A16_DMA + j) * A16_RPB + lane / A16_CH;
+        const int cA = (lane % A16_CH) ^ a16_phi(rowA);
         voffA[j] = rowA * lda * 2 + cA * 16;
         kchA[j] = cA * 8;
-        const int kB = blk * 2 + (lane >> 5);
+    }
+#pragma unroll
+    for (int j = 0; j < B16_DMA; ++j) {
+        const int kB = (wave * B16_DMA + j) * 2 + (lane >> 5);
         const int cB = (lane & 31) ^ b16_swz(kB);
         voffB[j] = kB * ldb * 2 + cB * 16;
     }
@@ -237,24 +255,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // empty ranges (they only keep the per-step load count uniform).
     auto issue_stage = [&](int kt) {
         const int s = kt % S16;
-        const int k0 = kt * BK;
+        const int k0 = kt * BK16;
         const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
         const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 2 : 0;
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
-        const int rows_b = krem < BK ? krem : BK;
+        const int rows_b = krem < BK16 ? krem : BK16;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 2;
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 2 : 0;
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < A16_DMA; ++j) {
             // A chunks wholly past K read as zero (a straddling chunk is fixed in LDS).
             const int off = (kchA[j] < krem) ? voffA[j] : (int)OOB;
-            dma16(rsa, lds_addr(smA + s * A16_STAGE + (wave * 4 + j) * 1024), off);
+            dma16(rsa, lds_addr(smA + s * A16_STAGE + (wave * A16_DMA + j) * 1024), off);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dma16(rsb, lds_addr(smB + s * B16_STAGE + (wave * 4 + j) * 1024), voffB[j]);
+        for (int j = 0; j < B16_DMA; ++j)
+            dma16(rsb, lds_addr(smB + s * B16_STAGE + (wave * B16_DMA + j) * 1024), voffB[j]);
     };
 
     // When K is not a multiple of 8, the last stage's A chunk that straddles K
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     auto fix_tail = [&]() {
         const int kt = nk - 1;
         const int s = kt % S16;
-        const int kin = K - kt * BK;         // valid k in the last stage, 1..31
+        const int kin = K - kt * BK16;       // valid k in the last stage, 1..BK16-1
         const int chunk = kin >> 3;          // the straddling chunk
         const int first = kin & 7;           // first invalid element in it
         short* p = (short*)(smA + s * A16_STAGE + a16_off(tid, chunk));
@@ -292,13 +310,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     u32x4 fa[2][4];
     s16x4 fb[2][4][2];
 
-    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
-        const int s = kt % S16;
-        const char* sa = smA + s * A16_STAGE;
-        const char* sb = smB + s * B16_STAGE;
+    auto read_frags_a = [&](int kt, int kp, u32x4 (&a)[4]) {
+        const char* sa = smA + (kt % S16) * A16_STAGE;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
             a[mi] = *(const u32x4*)(sa + a16_off(wm * 128 + mi * 32 + li, 2 * kp + g));
+    };
+    auto read_frags_b = [&](int kt, int kp, s16x4 (&b)[4][2]) {
+        const char* sb = smB + (kt % S16) * B16_STAGE;
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj) {
 #pragma unroll
@@ -310,24 +329,30 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
             }
         }
     };
+    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
+        read_frags_a(kt, kp, a);
+        read_frags_b(kt, kp, b);
+    };
 
-    auto mfma_frags = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2]) {
+    // One row of 32x32 blocks (mi) of a pair's 4 x 4 MFMAs.
+    auto mfma_row = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2], int mi) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj) {
-                const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                if constexpr (IN == IN_BF16) {
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, bv),
-                        acc[mi][nj], 0, 0, 0);
-                } else {
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv),
-                        acc[mi][nj], 0, 0, 0);
-                }
+        for (int nj = 0; nj < 4; ++nj) {
+            const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (IN == IN_BF16) {
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, bv),
+                    acc[mi][nj], 0, 0, 0);
+            } else {
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv),
+                    acc[mi][nj], 0, 0, 0);
             }
         }
+    };
+    auto mfma_frags = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) mfma_row(a, b, mi);
     };
 
     // Wait until at most VM of this wave's direct-to-LDS loads are in flight and
@@ -342,11 +367,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     using OneStepLeft = std::integral_constant<int, (S16 - 1) * LOADS16>;
     using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * LOADS16>;
 
-    // Schedule.  Prologue: loads of steps 0..3.  Step kt: read the fragments
-    // of pair 1 while pair 0's MFMAs run; wait for step kt + 1's loads (steps
-    // kt + 2, kt + 3 may still be in flight) and barrier, which also retires
-    // every wave's reads of stage kt % 4; refill that stage with step kt + 4;
-    // read pair 0 of step kt + 1 while pair 1's MFMAs of step kt run.
+    // Schedule (S16 stages, KP16 chunk pairs per step).  Prologue: loads of
+    // steps 0 .. S16 - 1.  Step kt: for pairs 0 .. KP16 - 2, read the next
+    // pair's fragments while this pair's MFMAs run; wait until step kt + 1
+    // has landed (later steps may still be in flight) and barrier, which also
+    // retires every wave's reads of stage kt % S16; then, between the last
+    // pair's MFMAs, refill that stage with step kt + S16 and read pair 0 of
+    // step kt + 1.
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < S16; ++s) issue_stage(s);
@@ -354,15 +381,32 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         if ((K & 7) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
-            read_frags(kt, 1, fa[1], fb[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[0], fb[0]);
+            // Pairs 0 .. KP16 - 2: read the next pair while this one computes.
+#pragma unroll
+            for (int kp = 0; kp + 1 < KP16; ++kp) {
+                read_frags(kt, kp + 1, fa[(kp + 1) & 1], fb[(kp + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_frags(fa[kp & 1], fb[kp & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             sync(TwoStepsLeft{});
             if ((K & 7) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            issue_stage(kt + S16);
-            if (kt + 1 < nk) read_frags(kt + 1, 0, fa[0], fb[0]);
+            // The last pair's fragments are ready: interleave its MFMAs with the
+            // refill and the next step's first reads so the matrix pipe stays busy.
+            constexpr int L = (KP16 - 1) & 1;
+            mfma_row(fa[L], fb[L], 0);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[1], fb[1]);
+            issue_stage(kt + S16);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_row(fa[L], fb[L], 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) read_frags_a(kt + 1, 0, fa[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_row(fa[L], fb[L], 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) read_frags_b(kt + 1, 0, fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_row(fa[L], fb[L], 3);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
