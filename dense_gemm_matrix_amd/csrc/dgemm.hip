@@ -251,28 +251,39 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         voffB[j] = kB * ldb * 2 + cB * 16;
     }
 
-    // Global loads of step kt into LDS stage kt % S16.  Steps past the end get
-    // empty ranges (they only keep the per-step load count uniform).
-    auto issue_stage = [&](int kt) {
-        const int s = kt % S16;
+    // Global loads of step kt into LDS stage kt % S16, one instruction at a
+    // time: stage_desc computes the step's two descriptors, dma_one(j) issues
+    // load j (A loads first, then B).  Steps past the end get empty ranges
+    // (they only keep the per-step load count uniform).
+    struct StageDesc { __amdgpu_buffer_rsrc_t ra, rb; int s, krem; };
+    auto stage_desc = [&](int kt) {
+        StageDesc d;
+        d.s = kt % S16;
         const int k0 = kt * BK16;
-        const int krem = K - k0;
+        d.krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
-        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 2 : 0;
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
-        const int rows_b = krem < BK16 ? krem : BK16;
+        const int64_t abytes = d.krem > 0 ? ((int64_t)(rows_a - 1) * lda + d.krem) * 2 : 0;
+        d.ra = make_rsrc(abase, abytes);
+        const int rows_b = d.krem < BK16 ? d.krem : BK16;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 2;
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 2 : 0;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
-#pragma unroll
-        for (int j = 0; j < A16_DMA; ++j) {
+        d.rb = make_rsrc(bbase, bbytes);
+        return d;
+    };
+    auto dma_one = [&](const StageDesc& d, int j) {
+        if (j < A16_DMA) {
             // A chunks wholly past K read as zero (a straddling chunk is fixed in LDS).
-            const int off = (kchA[j] < krem) ? voffA[j] : (int)OOB;
-            dma16(rsa, lds_addr(smA + s * A16_STAGE + (wave * A16_DMA + j) * 1024), off);
+            const int off = (kchA[j] < d.krem) ? voffA[j] : (int)OOB;
+            dma16(d.ra, lds_addr(smA + d.s * A16_STAGE + (wave * A16_DMA + j) * 1024), off);
+        } else {
+            const int jb = j - A16_DMA;
+            dma16(d.rb, lds_addr(smB + d.s * B16_STAGE + (wave * B16_DMA + jb) * 1024), voffB[jb]);
         }
+    };
+    auto issue_stage = [&](int kt) {
+        const StageDesc d = stage_desc(kt);
 #pragma unroll
-        for (int j = 0; j < B16_DMA; ++j)
-            dma16(rsb, lds_addr(smB + s * B16_STAGE + (wave * B16_DMA + j) * 1024), voffB[j]);
+        for (int j = 0; j < LOADS16; ++j) dma_one(d, j);
     };
 
     // When K is not a multiple of 8, the last stage's A chunk that straddles K
@@ -310,49 +321,35 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     u32x4 fa[2][4];
     s16x4 fb[2][4][2];
 
-    auto read_frags_a = [&](int kt, int kp, u32x4 (&a)[4]) {
-        const char* sa = smA + (kt % S16) * A16_STAGE;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            a[mi] = *(const u32x4*)(sa + a16_off(wm * 128 + mi * 32 + li, 2 * kp + g));
-    };
-    auto read_frags_b = [&](int kt, int kp, s16x4 (&b)[4][2]) {
-        const char* sb = smB + (kt % S16) * B16_STAGE;
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = kp * 16 + 8 * g + 4 * h + ta;
-                const int c = wn * 16 + nj * 4 + 2 * tg + (tq >> 1);
-                b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_t*)(sb + b16_off(k, c) + (tq & 1) * 8));
-            }
+    // Fragment read number i (0..11) of pair kp of step kt: 4 A reads, then
+    // 8 B transpose reads (nj = (i - 4) / 2, half (i - 4) % 2).
+    auto read_piece = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2], int i) {
+        if (i < 4) {
+            const char* sa = smA + (kt % S16) * A16_STAGE;
+            a[i] = *(const u32x4*)(sa + a16_off(wm * 128 + i * 32 + li, 2 * kp + g));
+        } else {
+            const char* sb = smB + (kt % S16) * B16_STAGE;
+            const int nj = (i - 4) >> 1, h = (i - 4) & 1;
+            const int k = kp * 16 + 8 * g + 4 * h + ta;
+            const int c = wn * 16 + nj * 4 + 2 * tg + (tq >> 1);
+            b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)(sb + b16_off(k, c) + (tq & 1) * 8));
         }
     };
-    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
-        read_frags_a(kt, kp, a);
-        read_frags_b(kt, kp, b);
+    auto mfma_one = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2], int mi, int nj) {
+        const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (IN == IN_BF16) {
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, bv), acc[mi][nj], 0, 0, 0);
+        } else {
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv), acc[mi][nj], 0, 0, 0);
+        }
     };
 
-    // One row of 32x32 blocks (mi) of a pair's 4 x 4 MFMAs.
-    auto mfma_row = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2], int mi) {
+    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-            const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            if constexpr (IN == IN_BF16) {
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, a[mi]), __builtin_bit_cast(bf16x8, bv),
-                    acc[mi][nj], 0, 0, 0);
-            } else {
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv),
-                    acc[mi][nj], 0, 0, 0);
-            }
-        }
-    };
-    auto mfma_frags = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2]) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) mfma_row(a, b, mi);
+        for (int i = 0; i < 12; ++i) read_piece(kt, kp, a, b, i);
     };
 
     // Wait until at most VM of this wave's direct-to-LDS loads are in flight and
@@ -367,13 +364,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     using OneStepLeft = std::integral_constant<int, (S16 - 1) * LOADS16>;
     using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * LOADS16>;
 
-    // Schedule (S16 stages, KP16 chunk pairs per step).  Prologue: loads of
-    // steps 0 .. S16 - 1.  Step kt: for pairs 0 .. KP16 - 2, read the next
-    // pair's fragments while this pair's MFMAs run; wait until step kt + 1
-    // has landed (later steps may still be in flight) and barrier, which also
-    // retires every wave's reads of stage kt % S16; then, between the last
-    // pair's MFMAs, refill that stage with step kt + S16 and read pair 0 of
-    // step kt + 1.
+    // Schedule (S16 stages, KP16 chunk pairs per step), written out in issue
+    // order: with one wave per SIMD nothing else hides a stall, so every
+    // load and LDS read sits between two MFMAs (sched_barrier pins the order).
+    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: for pairs
+    // 0 .. KP16 - 2, one fragment read of the next pair after each MFMA; wait
+    // until step kt + 1 has landed (later steps may still be in flight) and
+    // barrier, which also retires every wave's reads of stage kt % S16; then,
+    // during the last pair, one load of step kt + S16 into that stage after
+    // each MFMA, followed by the reads of pair 0 of step kt + 1.
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < S16; ++s) issue_stage(s);
@@ -381,33 +380,33 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         if ((K & 7) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
-            // Pairs 0 .. KP16 - 2: read the next pair while this one computes.
+            // Pairs 0 .. KP16 - 2: one read of the next pair after each MFMA.
 #pragma unroll
             for (int kp = 0; kp + 1 < KP16; ++kp) {
-                read_frags(kt, kp + 1, fa[(kp + 1) & 1], fb[(kp + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                mfma_frags(fa[kp & 1], fb[kp & 1]);
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma_one(fa[kp & 1], fb[kp & 1], i >> 2, i & 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (i < 12) read_piece(kt, kp + 1, fa[(kp + 1) & 1], fb[(kp + 1) & 1], i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             sync(TwoStepsLeft{});
             if ((K & 7) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            // The last pair's fragments are ready: interleave its MFMAs with the
-            // refill and the next step's first reads so the matrix pipe stays busy.
+            // Last pair: after each MFMA one load of step kt + S16 into the stage
+            // just freed, then the reads of pair 0 of step kt + 1.
             constexpr int L = (KP16 - 1) & 1;
-            mfma_row(fa[L], fb[L], 0);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_stage(kt + S16);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_row(fa[L], fb[L], 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) read_frags_a(kt + 1, 0, fa[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_row(fa[L], fb[L], 2);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) read_frags_b(kt + 1, 0, fb[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_row(fa[L], fb[L], 3);
-            __builtin_amdgcn_sched_barrier(0);
+            const StageDesc d = stage_desc(kt + S16);
+            const bool more = kt + 1 < nk;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mfma_one(fa[L], fb[L], i >> 2, i & 3);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i < LOADS16) dma_one(d, i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (more && i >= 4) read_piece(kt + 1, 0, fa[0], fb[0], i - 4);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     // No direct-to-LDS write may still be in flight when the workgroup ends.
