@@ -66,7 +66,6 @@ constexpr int NTHREADS = 256;                 // 4 waves
 constexpr int GROUP_M = 4;                    // tile rows per strip in the tile walk
 constexpr int NUM_XCD = 8;                    // XCDs that workgroups are dealt across
 constexpr uint32_t BUF_WORD3 = 0x00020000u;   // raw buffer: 32-bit data format, no swizzle
-constexpr uint32_t OOB = 0x7ffffff0u;         // a buffer offset past any range: reads zero
 constexpr int64_t DESC_LIMIT = (int64_t)1 << 31;
 
 // K per step: 32 for both kernels (fp32: 128-byte LDS rows; 16-bit: 64-byte rows).
@@ -236,13 +235,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // lane l fetches the chunk that belongs in its slot.  Wave w fills the
     // blocks w * DMA .. (w + 1) * DMA - 1 of each operand's stage: for A,
     // A16_RPB rows of A16_CH chunks each; for B, 2 k-rows of 32 chunks each.
-    int voffA[A16_DMA], kchA[A16_DMA], voffB[B16_DMA];
+    int voffA[A16_DMA], voffB[B16_DMA];
 #pragma unroll
     for (int j = 0; j < A16_DMA; ++j) {
         const int rowA = (wave * A16_DMA + j) * A16_RPB + lane / A16_CH;
         const int cA = (lane % A16_CH) ^ a16_phi(rowA);
         voffA[j] = rowA * lda * 2 + cA * 16;
-        kchA[j] = cA * 8;
     }
 #pragma unroll
     for (int j = 0; j < B16_DMA; ++j) {
@@ -272,9 +270,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     };
     auto dma_one = [&](const StageDesc& d, int j) {
         if (j < A16_DMA) {
-            // A chunks wholly past K read as zero (a straddling chunk is fixed in LDS).
-            const int off = (kchA[j] < d.krem) ? voffA[j] : (int)OOB;
-            dma16(d.ra, lds_addr(smA + d.s * A16_STAGE + (wave * A16_DMA + j) * 1024), off);
+            dma16(d.ra, lds_addr(smA + d.s * A16_STAGE + (wave * A16_DMA + j) * 1024), voffA[j]);
         } else {
             const int jb = j - A16_DMA;
             dma16(d.rb, lds_addr(smB + d.s * B16_STAGE + (wave * B16_DMA + jb) * 1024), voffB[jb]);
@@ -286,17 +282,23 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         for (int j = 0; j < LOADS16; ++j) dma_one(d, j);
     };
 
-    // When K is not a multiple of 8, the last stage's A chunk that straddles K
-    // holds other data past K (row padding or the next row); zero it in LDS, so
-    // that 0 * (NaN or Inf) can never reach the sum.
+    // When K is not a multiple of BK16, the last stage's A columns at and past
+    // K hold other data (row padding, the next row, or zeros past the range);
+    // zero them in LDS so that 0 * (NaN or Inf) can never reach the sum.  B's
+    // rows past K are already zero (outside the descriptor's range).
     auto fix_tail = [&]() {
         const int kt = nk - 1;
         const int s = kt % S16;
         const int kin = K - kt * BK16;       // valid k in the last stage, 1..BK16-1
-        const int chunk = kin >> 3;          // the straddling chunk
-        const int first = kin & 7;           // first invalid element in it
-        short* p = (short*)(smA + s * A16_STAGE + a16_off(tid, chunk));
-        for (int e = first; e < 8; ++e) p[e] = 0;
+        const int chunk0 = kin >> 3;         // first chunk holding an invalid element
+        char* rowp = smA + s * A16_STAGE;
+        const int row = tid;                 // one A row per thread
+        if (kin & 7) {
+            short* p = (short*)(rowp + a16_off(row, chunk0));
+            for (int e = kin & 7; e < 8; ++e) p[e] = 0;
+        }
+        for (int c = chunk0 + ((kin & 7) ? 1 : 0); c < A16_CH; ++c)
+            *(u32x4*)(rowp + a16_off(row, c)) = u32x4{0u, 0u, 0u, 0u};
     };
 
     const int wm = wave >> 1;
@@ -315,11 +317,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
-    // Operand fragments of one 16-k chunk pair: A as 4 x 8 consecutive k of a
-    // row; B as 4 x (two transpose reads of 4 consecutive k of a column).  Two
-    // sets alternate so one pair's reads overlap the other pair's MFMAs.
-    u32x4 fa[2][4];
-    s16x4 fb[2][4][2];
+    // Operand fragments, one register set per chunk pair of a step: A as
+    // 4 x 8 consecutive k of a row; B as 4 x (two transpose reads of 4
+    // consecutive k of a column).
+    u32x4 fa[KP16][4];
+    s16x4 fb[KP16][4][2];
 
     // Fragment read number i (0..11) of pair kp of step kt: 4 A reads, then
     // 8 B transpose reads (nj = (i - 4) / 2, half (i - 4) % 2).
@@ -367,45 +369,51 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // Schedule (S16 stages, KP16 chunk pairs per step), written out in issue
     // order: with one wave per SIMD nothing else hides a stall, so every
     // load and LDS read sits between two MFMAs (sched_barrier pins the order).
-    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: for pairs
-    // 0 .. KP16 - 2, one fragment read of the next pair after each MFMA; wait
-    // until step kt + 1 has landed (later steps may still be in flight) and
-    // barrier, which also retires every wave's reads of stage kt % S16; then,
-    // during the last pair, one load of step kt + S16 into that stage after
-    // each MFMA, followed by the reads of pair 0 of step kt + 1.
+    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: during pair 0's MFMAs
+    // read the fragments of pairs 1 .. KP16 - 1 (one register set per pair);
+    // then wait until step kt + 1 has landed (later steps may still be in
+    // flight) and barrier, which retires every wave's reads of stage kt % S16;
+    // then, spread over the MFMAs of pairs 1 .. KP16 - 1, refill that stage
+    // with step kt + S16, and during the last pair read pair 0 of step kt + 1.
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < S16; ++s) issue_stage(s);
         sync(OneStepLeft{});
-        if ((K & 7) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
+        if ((K % BK16) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
-            // Pairs 0 .. KP16 - 2: one read of the next pair after each MFMA.
-#pragma unroll
-            for (int kp = 0; kp + 1 < KP16; ++kp) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    mfma_one(fa[kp & 1], fb[kp & 1], i >> 2, i & 3);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (i < 12) read_piece(kt, kp + 1, fa[(kp + 1) & 1], fb[(kp + 1) & 1], i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            sync(TwoStepsLeft{});
-            if ((K & 7) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            // Last pair: after each MFMA one load of step kt + S16 into the stage
-            // just freed, then the reads of pair 0 of step kt + 1.
-            constexpr int L = (KP16 - 1) & 1;
-            const StageDesc d = stage_desc(kt + S16);
-            const bool more = kt + 1 < nk;
+            // Pair 0: after each MFMA, reads of pairs 1 .. KP16 - 1.
+            constexpr int NR = 12 * (KP16 - 1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mfma_one(fa[L], fb[L], i >> 2, i & 3);
+                mfma_one(fa[0], fb[0], i >> 2, i & 3);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i < LOADS16) dma_one(d, i);
+#pragma unroll
+                for (int r = (i * NR) / 16; r < ((i + 1) * NR) / 16; ++r)
+                    read_piece(kt, 1 + r / 12, fa[1 + r / 12], fb[1 + r / 12], r % 12);
                 __builtin_amdgcn_sched_barrier(0);
-                if (more && i >= 4) read_piece(kt + 1, 0, fa[0], fb[0], i - 4);
-                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Every read of stage kt is now issued: retire them, wait for step
+            // kt + 1, barrier.  The stage is then free for step kt + S16.
+            const StageDesc d = stage_desc(kt + S16);
+            sync(TwoStepsLeft{});
+            if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
+            const bool more = kt + 1 < nk;
+            // Pairs 1 .. KP16 - 1: the refill spread over their MFMAs; the last
+            // pair also carries the reads of pair 0 of step kt + 1.
+            constexpr int EVERY = (16 * (KP16 - 1)) / LOADS16;
+#pragma unroll
+            for (int kp = 1; kp < KP16; ++kp) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma_one(fa[kp], fb[kp], i >> 2, i & 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int j = (kp - 1) * 16 + i;
+                    if (j % EVERY == 0 && j / EVERY < LOADS16) dma_one(d, j / EVERY);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kp == KP16 - 1 && more && i >= 4) read_piece(kt + 1, 0, fa[0], fb[0], i - 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
