@@ -19,12 +19,13 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 _c_int, _c_void_p = ctypes.c_int, ctypes.c_void_p
-_lib.gemm_f32.argtypes = [_c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_int,
-                          _c_void_p, _c_int, _c_void_p]
+for _f in (_lib.gemm_f32, _lib.gemm_f32_3xbf16):
+    _f.argtypes = [_c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_int,
+                   _c_void_p, _c_int, _c_void_p]
 for _f in (_lib.gemm_bf16, _lib.gemm_f16):
     _f.argtypes = [_c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_int,
                    _c_void_p, _c_int, _c_int, _c_void_p]
-for _f in (_lib.gemm_f32, _lib.gemm_bf16, _lib.gemm_f16):
+for _f in (_lib.gemm_f32, _lib.gemm_f32_3xbf16, _lib.gemm_bf16, _lib.gemm_f16):
     _f.restype = _c_int
 _lib.dgemm_status_string.argtypes = [_c_int]
 _lib.dgemm_status_string.restype = ctypes.c_char_p
@@ -42,7 +43,7 @@ DGEMM_ERR_DEVICE = 6
 DGEMM_ERR_LAUNCH = 7
 DGEMM_OUT_F32 = 0
 DGEMM_OUT_SAME = 1
-IN_CODES = {"f32": 0, "bf16": 1, "f16": 2}
+IN_CODES = {"f32": 0, "bf16": 1, "f16": 2, "f32x3": 3}
 
 
 class DgemmError(RuntimeError):
@@ -99,6 +100,17 @@ def gemm_f32(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> 
     with torch.cuda.device(C.device):
         _check(_lib.gemm_f32(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(), _pitch(B, N),
                              C.data_ptr(), _pitch(C, N), _stream(C, stream)))
+
+
+def gemm_f32_3xbf16(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> None:
+    """C = A @ B for fp32 A, B, C on bf16 matrix units (each input split in two
+    bf16 parts, three products per term); error within 1e-4 * sum|a*b|."""
+    M, N, K = _shapes(A, B, C)
+    if not (A.dtype == B.dtype == C.dtype == torch.float32):
+        raise TypeError("gemm_f32_3xbf16 takes float32 A, B and C")
+    with torch.cuda.device(C.device):
+        _check(_lib.gemm_f32_3xbf16(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(),
+                                    _pitch(B, N), C.data_ptr(), _pitch(C, N), _stream(C, stream)))
 
 
 def _gemm16(fn, dtype, A, B, C, stream):

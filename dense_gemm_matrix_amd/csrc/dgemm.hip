@@ -57,7 +57,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-enum InFmt { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
+enum InFmt { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2, IN_F32X3 = 3 };  // F32X3: fp32 via 3 x bf16
 enum OutFmt { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
 constexpr int BM = 256;                       // macro-tile rows
@@ -71,7 +71,7 @@ constexpr int64_t DESC_LIMIT = (int64_t)1 << 31;
 // K per step: 32 for both kernels (fp32: 128-byte LDS rows; 16-bit: 64-byte rows).
 constexpr int BK = 32;
 
-int in_esize(int in) { return in == IN_F32 ? 4 : 2; }
+int in_esize(int in) { return (in == IN_F32 || in == IN_F32X3) ? 4 : 2; }
 
 // Workgroup -> output tile.  Step 1: workgroups are dealt to XCDs in turn, so
 // wg % 8 is its XCD; give XCD x the contiguous run of tile indices
@@ -592,6 +592,207 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     store_tile<OUT_F32>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li);
 }
 
+// ---------------------------------------------------------------- fp32 via 3 x bf16
+
+// fp32 inputs split into two bf16 parts, x = hi + lo + e with hi = bf16(x),
+// lo = bf16(x - hi) (both round to nearest even; x - hi is exact in fp32), so
+// |e| <= 2^-16 |x|.  a * b is taken as ah*bh + ah*bl + al*bh: the dropped
+// al*bl and the two truncations leave a relative error of at most about
+// 3 * 2^-16 per product, before fp32 accumulation.  Three bf16 MFMAs per
+// product at 8x the fp32 MFMA rate.
+//
+// Operands are staged through registers: each thread loads fp32 pieces of A
+// (8 consecutive k of one row) and B (an 8 k x 4 column block), splits them,
+// and writes hi and lo parts to LDS as K-contiguous bf16 rows (B is transposed
+// on the way, by its choice of which values to pack), so both operands are
+// read with ds_read_b128.  Double-buffered LDS, BK = 32.
+
+constexpr int X3_ROW = BK * 2;                  // 64-byte bf16 rows: 4 chunks
+constexpr int X3_PART = BM * X3_ROW;            // one part of one operand: 16 KiB
+constexpr int X3_STAGE = 4 * X3_PART;           // A hi, A lo, B hi, B lo: 64 KiB
+
+__device__ __forceinline__ int x3_off(int row, int chunk) {
+    return row * X3_ROW + ((chunk ^ ((row ^ (row >> 2)) & 3)) << 4);
+}
+
+// Split 8 fp32 values into packed hi and lo bf16 parts (element i in the low
+// half of word i / 2 when i is even).
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const __bf16 h0 = (__bf16)x[2 * w], h1 = (__bf16)x[2 * w + 1];
+        const __bf16 l0 = (__bf16)(x[2 * w] - (float)h0);
+        const __bf16 l1 = (__bf16)(x[2 * w + 1] - (float)h1);
+        hi[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo[w] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+}
+
+__global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * X3_STAGE];
+
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int nk = (K + BK - 1) / BK;
+    const bool ragged_k = (K % BK) != 0;
+
+    // A staging: thread -> 8 consecutive k (two 16-byte fp32 pieces) of rows
+    // ar0 + 64 i, i = 0..3, k chunk ac.
+    const int ac = tid & 3;
+    const int ar0 = tid >> 2;
+    // B staging: thread -> an 8 k x 4 column block (k rows 8 kb .., columns 4 nb ..).
+    const int kb = tid & 3;
+    const int nb = tid >> 2;
+
+    int voff_a[4], voff_b[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff_a[i] = (ar0 + 64 * i) * lda * 4 + ac * 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
+
+    u32x4 ra[8], rb[8];
+
+    auto load_step = [&](int kt, bool tail) {
+        const int k0 = kt * BK;
+        const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
+        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
+        const int rows_b = (K - k0) < BK ? (K - k0) : BK;
+        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
+        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ra[2 * i] = load16(rsa, voff_a[i]);
+            ra[2 * i + 1] = load16(rsa, voff_a[i] + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        if (tail) {
+            // Columns of A at or past K hold other data (row padding or the next
+            // row); they must be exact zeros, since the matching B rows are.
+            const int valid = K - k0 - ac * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[2 * i] = mask_tail32(ra[2 * i], valid);
+                ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
+            }
+        }
+    };
+
+    auto store_step = [&](int s) {
+        char* st = smem + s * X3_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = as_float(ra[2 * i][e]);
+                x[4 + e] = as_float(ra[2 * i + 1][e]);
+            }
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            const int off = x3_off(ar0 + 64 * i, ac);
+            *(u32x4*)(st + off) = hi;
+            *(u32x4*)(st + X3_PART + off) = lo;
+        }
+        // B: column cc of the block, 8 consecutive k -> one chunk per part.
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = as_float(rb[e][cc]);
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            const int off = x3_off(nb * 4 + cc, kb);
+            *(u32x4*)(st + 2 * X3_PART + off) = hi;
+            *(u32x4*)(st + 3 * X3_PART + off) = lo;
+        }
+    };
+
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    // Fragments of one 16-k chunk pair: [part][block], part 0 = hi, 1 = lo.
+    u32x4 fa[2][2][4], fb[2][2][4];
+
+    auto read_frags = [&](int s, int kp, u32x4 (&a)[2][4], u32x4 (&b)[2][4]) {
+        const char* st = smem + s * X3_STAGE;
+        const int ch = 2 * kp + g;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                a[p][mi] = *(const u32x4*)(st + p * X3_PART + x3_off(wm * 128 + mi * 32 + li, ch));
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                b[p][nj] = *(const u32x4*)(st + (2 + p) * X3_PART + x3_off(wn * 128 + nj * 32 + li, ch));
+        }
+    };
+
+    auto mfma_frags = [&](const u32x4 (&a)[2][4], const u32x4 (&b)[2][4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj) {
+                // small terms first, then the leading one
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[1][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[1][nj]), acc[mi][nj], 0, 0, 0);
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
+            }
+        }
+    };
+
+    // Per step: global loads of step kt + 1 -> registers; read pair 1 while
+    // pair 0 computes; split and write step kt + 1 to the other stage;
+    // barrier; read pair 0 of step kt + 1 while pair 1 computes.
+    if (nk > 0) {
+        load_step(0, ragged_k && nk == 1);
+        store_step(0);
+        __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
+            read_frags(cur, 1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) store_step(cur ^ 1);
+            __syncthreads();
+            if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    store_tile<OUT_F32>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li);
+}
+
 // ---------------------------------------------------------------- host side
 
 std::atomic<int> g_device_state[256];  // 0 unknown, 1 gfx950, 2 other
@@ -659,6 +860,8 @@ int launch(int M, int N, int K, const void* A, int lda, const void* B, int ldb, 
     const void* fn;
     if constexpr (IN == IN_F32)
         fn = (const void*)gemm32_kernel;
+    else if constexpr (IN == IN_F32X3)
+        fn = (const void*)gemm32x3_kernel;
     else
         fn = (const void*)gemm16_kernel<IN, OUT>;
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)ntiles),
@@ -678,7 +881,9 @@ int gemm_entry(int M, int N, int K, const void* A, int lda, const void* B, int l
     st = check_device();
     if (st != DGEMM_OK) return st;
     if (out == DGEMM_OUT_F32) return launch<IN, OUT_F32>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
-    if constexpr (IN == IN_BF16)
+    if constexpr (IN == IN_F32 || IN == IN_F32X3)
+        return DGEMM_ERR_INVALID_VALUE;  // fp32 inputs always give fp32 C
+    else if constexpr (IN == IN_BF16)
         return launch<IN_BF16, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
     else
         return launch<IN_F16, OUT_F16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
@@ -691,6 +896,11 @@ extern "C" {
 int gemm_f32(int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
              int ldc, void* stream) {
     return gemm_entry<IN_F32>(M, N, K, A, lda, B, ldb, C, ldc, DGEMM_OUT_F32, stream);
+}
+
+int gemm_f32_3xbf16(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
+                    float* C, int ldc, void* stream) {
+    return gemm_entry<IN_F32X3>(M, N, K, A, lda, B, ldb, C, ldc, DGEMM_OUT_F32, stream);
 }
 
 int gemm_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C,
@@ -719,7 +929,7 @@ const char* dgemm_status_string(int status) {
 
 int dgemm_tile_map(int M, int N, int in, int wg, int* tile_rows, int* tile_cols, int* num_wg,
                    int* tile_m, int* tile_n) {
-    if (M < 0 || N < 0 || (in != IN_F32 && in != IN_BF16 && in != IN_F16))
+    if (M < 0 || N < 0 || (in != IN_F32 && in != IN_BF16 && in != IN_F16 && in != IN_F32X3))
         return DGEMM_ERR_INVALID_VALUE;
     const int64_t tm_count = ((int64_t)M + BM - 1) / BM;
     const int64_t tn_count = ((int64_t)N + BN - 1) / BN;

@@ -73,6 +73,23 @@ int gemm_f32(int M, int N, int K,
              void* stream);
 
 /*
+ * fp32 inputs, fp32 C, computed with bf16 matrix instructions: each input is
+ * split as x = hi + lo (+ e) with hi = bf16(x), lo = bf16(x - hi), |e| <=
+ * 2^-16 |x|, and a*b is taken as hi*hi + hi*lo + lo*hi, accumulated in fp32
+ * (three v_mfma_f32_32x32x16_bf16 per product, at 8x the fp32 matrix rate).
+ * Per product the relative error is at most about 3 * 2^-16; results stay
+ * within 1e-4 * sum_k |a_ik * b_kj| of the exact product.  This is the
+ * MI355X counterpart of the sgemm tf32 page's approach (fp32 data on
+ * reduced-precision tensor units), more accurate than TF32's 10-bit inputs.
+ * Arguments, layout, errors and execution as gemm_f32.
+ */
+int gemm_f32_3xbf16(int M, int N, int K,
+                    const float* A, int lda,
+                    const float* B, int ldb,
+                    float* C, int ldc,
+                    void* stream);
+
+/*
  * bf16 inputs (raw 16-bit storage), fp32 accumulation, C fp32 (out =
  * DGEMM_OUT_F32) or bf16 (out = DGEMM_OUT_SAME).  The hgemm page's workload
  * (section 0, M = N = K = 4096, bf16 in and out).
@@ -98,7 +115,8 @@ const char* dgemm_status_string(int status);
 /*
  * Host-side query of the kernel's work distribution, for tests and tuning; it
  * launches nothing and needs no GPU.  For a problem of M x N outputs and input
- * format `in` (0 = fp32, 1 = bf16, 2 = fp16), writes the macro-tile shape and
+ * format `in` (0 = fp32, 1 = bf16, 2 = fp16, 3 = fp32 via 3 x bf16), writes the
+ * macro-tile shape and
  * the number of workgroups, and, when wg is in [0, *num_wg), the output tile
  * (row block *tile_m, column block *tile_n) that workgroup `wg` computes.  The
  * mapping is a bijection from workgroups to tiles: it first gives each of the

@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("gemm_f32", "gemm_bf16", "gemm_f16", "dgemm_status_string", "dgemm_tile_map"):
+    for want in ("gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16", "dgemm_status_string",
+                 "dgemm_tile_map"):
         assert want in names
 
 
@@ -52,14 +53,14 @@ V = ctypes.c_void_p
 
 def call(fn, M, N, K, A, lda, B, ldb, C, ldc, out=0):
     lib = dg.raw()
-    if fn == "gemm_f32":
-        return lib.gemm_f32(M, N, K, V(A), lda, V(B), ldb, V(C), ldc, None)
+    if fn in ("gemm_f32", "gemm_f32_3xbf16"):
+        return getattr(lib, fn)(M, N, K, V(A), lda, V(B), ldb, V(C), ldc, None)
     return getattr(lib, fn)(M, N, K, V(A), lda, V(B), ldb, V(C), ldc, out, None)
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16"])
 def test_validation_errors(fn):
-    es = 4 if fn == "gemm_f32" else 2
+    es = 4 if fn.startswith("gemm_f32") else 2
     ok_ld = 64
     assert call(fn, -1, 8, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
     assert call(fn, 8, -1, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
@@ -67,7 +68,7 @@ def test_validation_errors(fn):
     assert call(fn, 8, 8, 8, 0, ok_ld, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
     assert call(fn, 8, 8, 8, PA, ok_ld, 0, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
     assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, 0, ok_ld) == dg.DGEMM_ERR_INVALID_VALUE
-    if fn != "gemm_f32":
+    if not fn.startswith("gemm_f32"):
         assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, PC, ok_ld, out=2) == dg.DGEMM_ERR_INVALID_VALUE
     assert call(fn, 8, 8, 72, PA, 64, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_LEADING_DIM
     assert call(fn, 8, 72, 8, PA, ok_ld, PB, 64, PC, 80) == dg.DGEMM_ERR_LEADING_DIM
@@ -89,7 +90,7 @@ def test_validation_errors(fn):
 
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16"])
 def test_empty_output_is_a_no_op_without_device(fn):
     # M == 0 or N == 0: nothing to write, no device needed, even with NULL pointers.
     assert call(fn, 0, 8, 8, 0, 8, 0, 8, 0, 8) == dg.DGEMM_OK
@@ -98,7 +99,7 @@ def test_empty_output_is_a_no_op_without_device(fn):
 
 @pytest.mark.parametrize("M,N", [(1, 1), (256, 256), (4096, 4096), (16384, 4096), (4000, 3000),
                                  (257, 4097), (2560, 256), (256, 9000), (7777, 3333), (512, 512)])
-@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f32x3"])
 def test_tile_map_is_a_bijection(M, N, fmt):
     info = dg.dgemm_tile_map(M, N, fmt)
     tm_n = -(-M // info["tile_rows"])

@@ -17,17 +17,25 @@ from tests.gpu_util import TORCH, dev_matrix, gap_untouched, round_pitch, sentin
 
 pytestmark = pytest.mark.gpu
 
-ENTRY = {"f32": dg.gemm_f32, "bf16": dg.gemm_bf16, "f16": dg.gemm_f16}
-COMBOS = [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")]
+# path -> entry point; "f32x3" is fp32 data through the 3 x bf16 split entry.
+ENTRY = {"f32": dg.gemm_f32, "f32x3": dg.gemm_f32_3xbf16, "bf16": dg.gemm_bf16, "f16": dg.gemm_f16}
+COMBOS = [("f32", "f32"), ("f32x3", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
+          ("f16", "f16")]
 
 
-def run(dtype, out, A, B, a_extra=0, b_extra=0, c_extra=4, stream=None):
+def store(path):
+    """Storage dtype of a path's inputs."""
+    return "f32" if path == "f32x3" else path
+
+
+def run(path, out, A, B, a_extra=0, b_extra=0, c_extra=4, stream=None):
     M, K = A.shape
     N = B.shape[1]
+    dtype = store(path)
     Ad = dev_matrix(A, dtype, round_pitch(K, dtype, a_extra))
     Bd = dev_matrix(B, dtype, round_pitch(N, dtype, b_extra))
     Cd = sentinel_c(M, N, out, round_pitch(N, out, c_extra))
-    ENTRY[dtype](Ad, Bd, Cd, stream=stream)
+    ENTRY[path](Ad, Bd, Cd, stream=stream)
     if stream is not None:
         stream.synchronize()
     torch.cuda.synchronize()
@@ -44,50 +52,56 @@ DIMS_MN = [1, 7, 33, 255, 256, 257]
 DIMS_K = [1, 7, 64, 65, 255, 257]
 
 
-@pytest.mark.parametrize("dtype,out", COMBOS)
-def test_small_and_ragged_shapes(dtype, out):
-    rng = np.random.default_rng(1000 + COMBOS.index((dtype, out)))
+@pytest.mark.parametrize("path,out", COMBOS)
+def test_small_and_ragged_shapes(path, out):
+    rng = np.random.default_rng(1000 + COMBOS.index((path, out)))
+    dtype = store(path)
     for M in DIMS_MN:
         for N in DIMS_MN:
             for K in DIMS_K:
-                print(f"case {dtype}->{out} {M}x{N}x{K}", flush=True)
+                print(f"case {path}->{out} {M}x{N}x{K}", flush=True)
                 A = draw(rng, (M, K), "normal", dtype)
                 B = draw(rng, (K, N), "normal", dtype)
-                C = run(dtype, out, A, B, a_extra=8, b_extra=8)
+                C = run(path, out, A, B, a_extra=8, b_extra=8)
                 C64, S = oracle.gemm(dtype, A, B)
                 res = oracle.check(to64(C), C64, S, TOL_MFMA, out)
                 assert res["ok"], (M, N, K, res)
                 assert gap_untouched(C), (M, N, K)
 
 
-@pytest.mark.parametrize("dtype,out", COMBOS)
+@pytest.mark.parametrize("path,out", COMBOS)
 @pytest.mark.parametrize("M,N,K", [(1000, 700, 1100), (512, 768, 4104), (300, 264, 200)])
-def test_exact_integer_inputs_bitwise(dtype, out, M, N, K):
+def test_exact_integer_inputs_bitwise(path, out, M, N, K):
     """Integers in [-8, 8]: every partial sum is an integer below 2^24, so the fp32
     accumulator is exact in any order; C must equal the oracle's C64 rounded once
     to C's format, bit for bit.  This pins tiling, staging, the LDS layout, the
     operand layouts, masking, the tile map and the epilogue."""
-    print(f"case int {dtype}->{out} {M}x{N}x{K}", flush=True)
+    print(f"case int {path}->{out} {M}x{N}x{K}", flush=True)
+    dtype = store(path)
     A, B = pair(M, N, K, "ints", dtype, seed=2000 + M + N + K)
-    C = run(dtype, out, A, B, a_extra=8, b_extra=16)
+    C = run(path, out, A, B, a_extra=8, b_extra=16)
     C64, _ = oracle.gemm(dtype, A, B)
     want = oracle.widen(out, oracle.round_to(out, C64))
     assert np.array_equal(to64(C), want)
     assert gap_untouched(C)
 
 
-@pytest.mark.parametrize("name", ["f32_512", "f32_4096", "bf16_4096", "f16_4096",
-                                  "bf16_16384x4096x4096", "bf16_4000x3000x4104"])
-def test_workloads(name):
-    """The six workloads at full size; the oracle checks sampled rows (all rows
-    at 512^3), and no element of C may be left unwritten."""
+@pytest.mark.parametrize("name,path", [("f32_512", "f32"), ("f32_4096", "f32"),
+                                       ("f32_512", "f32x3"), ("f32_4096", "f32x3"),
+                                       ("bf16_4096", "bf16"), ("f16_4096", "f16"),
+                                       ("bf16_16384x4096x4096", "bf16"),
+                                       ("bf16_4000x3000x4104", "bf16")])
+def test_workloads(name, path):
+    """The six workloads at full size (fp32 ones through both fp32 entry
+    points); the oracle checks sampled rows (all rows at 512^3), and no
+    element of C may be left unwritten."""
     A, B, meta = workload(name)
     dtype, out, M = meta["dtype"], meta["out"], meta["M"]
-    print(f"case workload {name}", flush=True)
+    print(f"case workload {name} via {path}", flush=True)
     Ad = dev_matrix(A, dtype, A.shape[1])
     Bd = dev_matrix(B, dtype, B.shape[1])
     Cd = torch.full((M, meta["N"]), float("nan"), dtype=TORCH[out], device="cuda")
-    ENTRY[dtype](Ad, Bd, Cd)
+    ENTRY[path](Ad, Bd, Cd)
     torch.cuda.synchronize()
     assert not bool(torch.isnan(Cd.float()).any().item()), "unwritten elements"
     rows = np.arange(M) if M <= 512 else sample_rows(M, np.random.default_rng(meta["seed"]))
@@ -99,16 +113,17 @@ def test_workloads(name):
     assert res["ok"], res
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_exact_integer_full_size_freivalds(dtype):
+@pytest.mark.parametrize("path", ["f32", "f32x3", "bf16", "f16"])
+def test_exact_integer_full_size_freivalds(path):
     """4096^3 with integer inputs and fp32 C: C is exact, so C.x == A.(B.x)
     exactly in fp64 for integer vectors x (all values stay below 2^53).  Three
     random x make a wrong element anywhere in C show with near certainty; rows
     sampled against the oracle pin the values themselves."""
     M = N = K = 4096
-    print(f"case freivalds {dtype}", flush=True)
+    print(f"case freivalds {path}", flush=True)
+    dtype = store(path)
     A, B = pair(M, N, K, "ints", dtype, seed=3000)
-    C = run(dtype, "f32", A, B)
+    C = run(path, "f32", A, B)
     Cn = to64(C)
     Aw = oracle.widen(dtype, A)
     Bw = oracle.widen(dtype, B)
@@ -139,27 +154,29 @@ def test_non_default_stream():
     assert torch.equal(ref, got)
 
 
-@pytest.mark.parametrize("dtype,out", COMBOS)
-def test_leading_dimensions_larger_than_rows(dtype, out):
+@pytest.mark.parametrize("path,out", COMBOS)
+def test_leading_dimensions_larger_than_rows(path, out):
+    dtype = store(path)
     A, B = pair(333, 290, 515, "normal", dtype, seed=4200)
-    C = run(dtype, out, A, B, a_extra=136, b_extra=264, c_extra=72)
+    C = run(path, out, A, B, a_extra=136, b_extra=264, c_extra=72)
     C64, S = oracle.gemm(dtype, A, B)
     assert oracle.check(to64(C), C64, S, TOL_MFMA, out)["ok"]
     assert gap_untouched(C)
 
 
-@pytest.mark.parametrize("dtype,out", COMBOS)
-def test_k_zero_writes_zeros_and_empty_outputs(dtype, out):
+@pytest.mark.parametrize("path,out", COMBOS)
+def test_k_zero_writes_zeros_and_empty_outputs(path, out):
+    dtype = store(path)
     A = np.zeros((300, 0), dtype=np.float32)
     Ad = torch.zeros((300, 8), dtype=TORCH[dtype], device="cuda")[:, :0]
     Bd = torch.zeros((1, 264), dtype=TORCH[dtype], device="cuda")[:0]
     C = sentinel_c(300, 264, out)
-    ENTRY[dtype](Ad, Bd, C)
+    ENTRY[path](Ad, Bd, C)
     torch.cuda.synchronize()
     assert bool((C.float() == 0).all().item()) and gap_untouched(C)
     assert A.shape[1] == 0
     C0 = torch.empty((0, 5), dtype=TORCH[out], device="cuda")
-    ENTRY[dtype](torch.zeros((0, 3), dtype=TORCH[dtype], device="cuda"),
+    ENTRY[path](torch.zeros((0, 3), dtype=TORCH[dtype], device="cuda"),
                  torch.zeros((3, 5), dtype=TORCH[dtype], device="cuda"), C0)
 
 
