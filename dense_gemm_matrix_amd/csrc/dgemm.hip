@@ -160,13 +160,13 @@ __device__ __forceinline__ void store_c(char* C, int64_t idx, float v) {
 
 // Epilogue shared by both kernels.  32x32 accumulator layout: lane (g, li)
 // holds column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4.
-template <int OUT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], char* C, int M, int N,
+template <int OUT, int MI = 4, int NJ = 4>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
                                            int ldc, int row0, int col0, int g, int li) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
+        for (int nj = 0; nj < NJ; ++nj) {
             const int col = col0 + nj * 32 + li;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -184,17 +184,31 @@ constexpr int S16 = 2;                         // LDS stages
 constexpr int KP16 = BK16 / 16;                // 16-k chunk pairs per stage
 constexpr int A16_CH = BK16 / 8;               // 16-byte chunks per A row
 constexpr int A16_ROW = BK16 * 2;              // bytes per staged A row
-constexpr int A16_STAGE = BM * A16_ROW;        // bytes per A stage
-constexpr int B16_ROW = BN * 2;                // 512 bytes: 32 chunks
-constexpr int B16_STAGE = BK16 * B16_ROW;      // bytes per B stage
-constexpr int A16_DMA = A16_STAGE / 1024 / 4;  // direct-to-LDS loads per wave per stage (A)
-constexpr int B16_DMA = B16_STAGE / 1024 / 4;  // ... (B)
-constexpr int LOADS16 = A16_DMA + B16_DMA;     // per thread per stage
 constexpr int A16_RPB = 1024 / A16_ROW;        // A rows per 1 KiB load block
-static_assert(S16 * (A16_STAGE + B16_STAGE) <= 160 * 1024, "LDS budget");
-static_assert((S16 - 1) * LOADS16 <= 63, "vmcnt range");
 
-// Byte offset of chunk c (0..3) of A row r in a stage.  ds_read_b128 serves
+// Macro-tile TBM x TBN, 4 waves in a 2 x 2 layout, each wave (TBM/2) x (TBN/2)
+// = MI x NJ blocks of 32 x 32 accumulators.
+template <int TBM, int TBN>
+struct Tile16 {
+    static constexpr int MI = TBM / 64;
+    static constexpr int NJ = TBN / 64;
+    static constexpr int A_STAGE = TBM * A16_ROW;        // bytes per A stage
+    static constexpr int B_ROW = TBN * 2;                // bytes per staged B row
+    static constexpr int B_CH = TBN / 8;                 // 16-byte chunks per B row
+    static constexpr int B_STAGE = BK16 * B_ROW;         // bytes per B stage
+    static constexpr int B_RPB = 1024 / B_ROW;           // B rows per 1 KiB load block
+    static constexpr int A_DMA = A_STAGE / 1024 / 4;     // direct-to-LDS loads per wave per stage
+    static constexpr int B_DMA = B_STAGE / 1024 / 4;
+    static constexpr int LOADS = A_DMA + B_DMA;
+    static constexpr int NREAD = MI + 2 * NJ;            // fragment reads per chunk pair
+    static constexpr int NMFMA = MI * NJ;                // MFMAs per chunk pair
+    static_assert(TBM % 64 == 0 && TBN % 64 == 0 && TBM <= NTHREADS, "tile shape");
+    static_assert(A_STAGE % 4096 == 0 && B_STAGE % 4096 == 0, "whole load blocks per wave");
+    static_assert(S16 * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
+    static_assert((S16 - 1) * LOADS <= 63, "vmcnt range");
+};
+
+// Byte offset of chunk c (0..7) of A row r in a stage.  ds_read_b128 serves
 // groups of 4 consecutive lanes from a 64-byte window of banks (measured on
 // gfx950 with SQ_LDS_BANK_CONFLICT), and the 4 lanes of a group read 4
 // consecutive rows at one chunk: a16_phi gives those rows 4 distinct slots.
@@ -202,50 +216,52 @@ __device__ __forceinline__ int a16_phi(int row) { return (row ^ (row >> 2)) & (A
 __device__ __forceinline__ int a16_off(int row, int chunk) {
     return row * A16_ROW + ((chunk ^ a16_phi(row)) << 4);
 }
-// Byte offset of chunk c (0..31) of B row k in a stage.  ds_read_b64_tr_b16
-// serves 32 lanes from a 256-byte window (measured), and those 32 lanes read 4
-// consecutive k rows x 64 bytes; the XOR puts the four rows' pieces in
-// distinct quarters of the window.
+// Byte offset of chunk c of B row k in a stage with row pitch `row_bytes` (a
+// multiple of 256).  ds_read_b64_tr_b16 serves 32 lanes from a 256-byte
+// window (measured), and those 32 lanes read 4 consecutive k rows x 64 bytes;
+// the XOR puts the four rows' pieces in distinct quarters of the window.
 __device__ __forceinline__ int b16_swz(int k) { return ((k & 3) << 1) ^ ((k & 1) << 3); }
-__device__ __forceinline__ int b16_off(int k, int chunk) {
-    return k * B16_ROW + ((chunk ^ b16_swz(k)) << 4);
+__device__ __forceinline__ int b16_off(int k, int chunk, int row_bytes) {
+    return k * row_bytes + ((chunk ^ b16_swz(k)) << 4);
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, int TBM, int TBN>
 __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) char smem[S16 * (A16_STAGE + B16_STAGE)];
+    using T = Tile16<TBM, TBN>;
+    constexpr int MI = T::MI, NJ = T::NJ;
+    __shared__ __attribute__((aligned(1024))) char smem[S16 * (T::A_STAGE + T::B_STAGE)];
     char* const smA = smem;
-    char* const smB = smem + S16 * A16_STAGE;
+    char* const smB = smem + S16 * T::A_STAGE;
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
-    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int m0 = tm * TBM;
+    const int n0 = tn * TBN;
+    const int rows_a = (M - m0) < TBM ? (M - m0) : TBM;
+    const int cols_b = (N - n0) < TBN ? (N - n0) : TBN;
     const int nk = (K + BK16 - 1) / BK16;
 
     // Each direct-to-LDS instruction fills a 1 KiB block lane-linearly (lane l
     // -> bytes 16 l .. 16 l + 15), so the swizzle is applied on the global side:
     // lane l fetches the chunk that belongs in its slot.  Wave w fills the
     // blocks w * DMA .. (w + 1) * DMA - 1 of each operand's stage: for A,
-    // A16_RPB rows of A16_CH chunks each; for B, 2 k-rows of 32 chunks each.
-    int voffA[A16_DMA], voffB[B16_DMA];
+    // A16_RPB rows of A16_CH chunks each; for B, B_RPB k-rows of B_CH chunks.
+    int voffA[T::A_DMA], voffB[T::B_DMA];
 #pragma unroll
-    for (int j = 0; j < A16_DMA; ++j) {
-        const int rowA = (wave * A16_DMA + j) * A16_RPB + lane / A16_CH;
+    for (int j = 0; j < T::A_DMA; ++j) {
+        const int rowA = (wave * T::A_DMA + j) * A16_RPB + lane / A16_CH;
         const int cA = (lane % A16_CH) ^ a16_phi(rowA);
         voffA[j] = rowA * lda * 2 + cA * 16;
     }
 #pragma unroll
-    for (int j = 0; j < B16_DMA; ++j) {
-        const int kB = (wave * B16_DMA + j) * 2 + (lane >> 5);
-        const int cB = (lane & 31) ^ b16_swz(kB);
+    for (int j = 0; j < T::B_DMA; ++j) {
+        const int kB = (wave * T::B_DMA + j) * T::B_RPB + lane / T::B_CH;
+        const int cB = (lane % T::B_CH) ^ b16_swz(kB);
         voffB[j] = kB * ldb * 2 + cB * 16;
     }
 
@@ -253,33 +269,33 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // time: stage_desc computes the step's two descriptors, dma_one(j) issues
     // load j (A loads first, then B).  Steps past the end get empty ranges
     // (they only keep the per-step load count uniform).
-    struct StageDesc { __amdgpu_buffer_rsrc_t ra, rb; int s, krem; };
+    struct StageDesc { __amdgpu_buffer_rsrc_t ra, rb; int s; };
     auto stage_desc = [&](int kt) {
         StageDesc d;
         d.s = kt % S16;
         const int k0 = kt * BK16;
-        d.krem = K - k0;
+        const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
-        const int64_t abytes = d.krem > 0 ? ((int64_t)(rows_a - 1) * lda + d.krem) * 2 : 0;
+        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 2 : 0;
         d.ra = make_rsrc(abase, abytes);
-        const int rows_b = d.krem < BK16 ? d.krem : BK16;
+        const int rows_b = krem < BK16 ? krem : BK16;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 2;
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 2 : 0;
         d.rb = make_rsrc(bbase, bbytes);
         return d;
     };
     auto dma_one = [&](const StageDesc& d, int j) {
-        if (j < A16_DMA) {
-            dma16(d.ra, lds_addr(smA + d.s * A16_STAGE + (wave * A16_DMA + j) * 1024), voffA[j]);
+        if (j < T::A_DMA) {
+            dma16(d.ra, lds_addr(smA + d.s * T::A_STAGE + (wave * T::A_DMA + j) * 1024), voffA[j]);
         } else {
-            const int jb = j - A16_DMA;
-            dma16(d.rb, lds_addr(smB + d.s * B16_STAGE + (wave * B16_DMA + jb) * 1024), voffB[jb]);
+            const int jb = j - T::A_DMA;
+            dma16(d.rb, lds_addr(smB + d.s * T::B_STAGE + (wave * T::B_DMA + jb) * 1024), voffB[jb]);
         }
     };
     auto issue_stage = [&](int kt) {
         const StageDesc d = stage_desc(kt);
 #pragma unroll
-        for (int j = 0; j < LOADS16; ++j) dma_one(d, j);
+        for (int j = 0; j < T::LOADS; ++j) dma_one(d, j);
     };
 
     // When K is not a multiple of BK16, the last stage's A columns at and past
@@ -291,14 +307,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         const int s = kt % S16;
         const int kin = K - kt * BK16;       // valid k in the last stage, 1..BK16-1
         const int chunk0 = kin >> 3;         // first chunk holding an invalid element
-        char* rowp = smA + s * A16_STAGE;
+        char* rowp = smA + s * T::A_STAGE;
         const int row = tid;                 // one A row per thread
-        if (kin & 7) {
-            short* p = (short*)(rowp + a16_off(row, chunk0));
-            for (int e = kin & 7; e < 8; ++e) p[e] = 0;
+        if (row < TBM) {
+            if (kin & 7) {
+                short* p = (short*)(rowp + a16_off(row, chunk0));
+                for (int e = kin & 7; e < 8; ++e) p[e] = 0;
+            }
+            for (int c = chunk0 + ((kin & 7) ? 1 : 0); c < A16_CH; ++c)
+                *(u32x4*)(rowp + a16_off(row, c)) = u32x4{0u, 0u, 0u, 0u};
         }
-        for (int c = chunk0 + ((kin & 7) ? 1 : 0); c < A16_CH; ++c)
-            *(u32x4*)(rowp + a16_off(row, c)) = u32x4{0u, 0u, 0u, 0u};
     };
 
     const int wm = wave >> 1;
@@ -309,36 +327,36 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     const int tq = lane & 3;          // transpose read: source 4-column piece
     const int tg = (lane >> 4) & 1;   // transpose read: the 16-lane group's column half
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
+        for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
     // Operand fragments, one register set per chunk pair of a step: A as
-    // 4 x 8 consecutive k of a row; B as 4 x (two transpose reads of 4
+    // MI x 8 consecutive k of a row; B as NJ x (two transpose reads of 4
     // consecutive k of a column).
-    u32x4 fa[KP16][4];
-    s16x4 fb[KP16][4][2];
+    u32x4 fa[KP16][MI];
+    s16x4 fb[KP16][NJ][2];
 
-    // Fragment read number i (0..11) of pair kp of step kt: 4 A reads, then
-    // 8 B transpose reads (nj = (i - 4) / 2, half (i - 4) % 2).
-    auto read_piece = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2], int i) {
-        if (i < 4) {
-            const char* sa = smA + (kt % S16) * A16_STAGE;
-            a[i] = *(const u32x4*)(sa + a16_off(wm * 128 + i * 32 + li, 2 * kp + g));
+    // Fragment read number i (0 .. NREAD - 1) of pair kp of step kt: MI A
+    // reads, then 2 NJ B transpose reads (nj = (i - MI) / 2, half (i - MI) % 2).
+    auto read_piece = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2], int i) {
+        if (i < MI) {
+            const char* sa = smA + (kt % S16) * T::A_STAGE;
+            a[i] = *(const u32x4*)(sa + a16_off(wm * (TBM / 2) + i * 32 + li, 2 * kp + g));
         } else {
-            const char* sb = smB + (kt % S16) * B16_STAGE;
-            const int nj = (i - 4) >> 1, h = (i - 4) & 1;
+            const char* sb = smB + (kt % S16) * T::B_STAGE;
+            const int nj = (i - MI) >> 1, h = (i - MI) & 1;
             const int k = kp * 16 + 8 * g + 4 * h + ta;
-            const int c = wn * 16 + nj * 4 + 2 * tg + (tq >> 1);
+            const int c = wn * (TBN / 16) + nj * 4 + 2 * tg + (tq >> 1);
             b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t*)(sb + b16_off(k, c) + (tq & 1) * 8));
+                (lds_s16x4_t*)(sb + b16_off(k, c, T::B_ROW) + (tq & 1) * 8));
         }
     };
-    auto mfma_one = [&](const u32x4 (&a)[4], const s16x4 (&b)[4][2], int mi, int nj) {
+    auto mfma_one = [&](const u32x4 (&a)[MI], const s16x4 (&b)[NJ][2], int mi, int nj) {
         const s16x8 bv = __builtin_shufflevector(b[nj][0], b[nj][1], 0, 1, 2, 3, 4, 5, 6, 7);
         if constexpr (IN == IN_BF16) {
             acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -348,10 +366,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
                 __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv), acc[mi][nj], 0, 0, 0);
         }
     };
-
-    auto read_frags = [&](int kt, int kp, u32x4 (&a)[4], s16x4 (&b)[4][2]) {
+    auto read_frags = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2]) {
 #pragma unroll
-        for (int i = 0; i < 12; ++i) read_piece(kt, kp, a, b, i);
+        for (int i = 0; i < T::NREAD; ++i) read_piece(kt, kp, a, b, i);
     };
 
     // Wait until at most VM of this wave's direct-to-LDS loads are in flight and
@@ -363,8 +380,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    using OneStepLeft = std::integral_constant<int, (S16 - 1) * LOADS16>;
-    using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * LOADS16>;
+    using OneStepLeft = std::integral_constant<int, (S16 - 1) * T::LOADS>;
+    using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * T::LOADS>;
 
     // Schedule (S16 stages, KP16 chunk pairs per step), written out in issue
     // order: with one wave per SIMD nothing else hides a stall, so every
@@ -382,15 +399,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         if ((K % BK16) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
-            // Pair 0: after each MFMA, reads of pairs 1 .. KP16 - 1.
-            constexpr int NR = 12 * (KP16 - 1);
+            constexpr int NR = T::NREAD * (KP16 - 1);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                mfma_one(fa[0], fb[0], i >> 2, i & 3);
+            for (int i = 0; i < T::NMFMA; ++i) {
+                mfma_one(fa[0], fb[0], i / NJ, i % NJ);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int r = (i * NR) / 16; r < ((i + 1) * NR) / 16; ++r)
-                    read_piece(kt, 1 + r / 12, fa[1 + r / 12], fb[1 + r / 12], r % 12);
+                for (int r = (i * NR) / T::NMFMA; r < ((i + 1) * NR) / T::NMFMA; ++r)
+                    read_piece(kt, 1 + r / T::NREAD, fa[1 + r / T::NREAD], fb[1 + r / T::NREAD],
+                               r % T::NREAD);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // Every read of stage kt is now issued: retire them, wait for step
@@ -399,19 +416,23 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
             sync(TwoStepsLeft{});
             if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
             const bool more = kt + 1 < nk;
-            // Pairs 1 .. KP16 - 1: the refill spread over their MFMAs; the last
-            // pair also carries the reads of pair 0 of step kt + 1.
-            constexpr int EVERY = (16 * (KP16 - 1)) / LOADS16;
+            constexpr int SLOTS = T::NMFMA * (KP16 - 1);
 #pragma unroll
             for (int kp = 1; kp < KP16; ++kp) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    mfma_one(fa[kp], fb[kp], i >> 2, i & 3);
+                for (int i = 0; i < T::NMFMA; ++i) {
+                    mfma_one(fa[kp], fb[kp], i / NJ, i % NJ);
                     __builtin_amdgcn_sched_barrier(0);
-                    const int j = (kp - 1) * 16 + i;
-                    if (j % EVERY == 0 && j / EVERY < LOADS16) dma_one(d, j / EVERY);
+                    const int slot = (kp - 1) * T::NMFMA + i;
+#pragma unroll
+                    for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
+                        dma_one(d, j);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (kp == KP16 - 1 && more && i >= 4) read_piece(kt + 1, 0, fa[0], fb[0], i - 4);
+                    if (kp == KP16 - 1 && more) {
+#pragma unroll
+                        for (int r = (i * T::NREAD) / T::NMFMA; r < ((i + 1) * T::NREAD) / T::NMFMA; ++r)
+                            read_piece(kt + 1, 0, fa[0], fb[0], r);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -420,7 +441,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // No direct-to-LDS write may still be in flight when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-    store_tile<OUT>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li);
+    store_tile<OUT, MI, NJ>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / 2), g, li);
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -816,7 +837,7 @@ bool ranges_overlap(uintptr_t a0, int64_t alen, uintptr_t b0, int64_t blen) {
 }
 
 int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
-             int ldc, int in, int es_out, int64_t* ntiles_out) {
+             int ldc, int in, int es_out) {
     const int es = in_esize(in);
     if (M < 0 || N < 0 || K < 0) return DGEMM_ERR_INVALID_VALUE;
     const bool writes = M > 0 && N > 0;
@@ -842,30 +863,66 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
     // with 32-bit offsets.
     if ((int64_t)BM * lda * es >= DESC_LIMIT || (int64_t)BK * ldb * es >= DESC_LIMIT)
         return DGEMM_ERR_TOO_LARGE;
-    const int64_t tiles = ((int64_t)(M + BM - 1) / BM) * ((int64_t)(N + BN - 1) / BN);
-    if (tiles > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
-    *ntiles_out = tiles;
     return DGEMM_OK;
+}
+
+// Macro-tile choice for the 16-bit kernel: the candidate minimising the
+// estimated time ceil(tiles / CUs) x tile_area / efficiency, where the
+// efficiencies (256 x 256: 1, 192 x 256: 0.95, 128 x 128: 0.6) are rough
+// measured ratios of per-tile throughput.  Large grids keep 256 x 256; grids
+// that would leave CUs idle (4000 x 3000: 192 tiles of 256^2 against 252 of
+// 192 x 256) or that have few tiles (512^2) move to smaller tiles.  fp32
+// kernels use 256 x 256 only.  Fixed CU count: the choice does not depend on
+// the device, so the host query below reports exactly what a launch uses.
+constexpr int NUM_CU = 256;
+
+struct TileChoice { int bm, bn; };
+
+TileChoice pick_tile(int in, int M, int N) {
+    if (in == IN_F32 || in == IN_F32X3) return {BM, BN};
+    const struct { int bm, bn; double eff; } cand[] = {{256, 256, 1.0}, {192, 256, 0.95}, {128, 128, 0.6}};
+    TileChoice best{256, 256};
+    double best_cost = -1.0;
+    for (const auto& c : cand) {
+        const int64_t tiles = (((int64_t)M + c.bm - 1) / c.bm) * (((int64_t)N + c.bn - 1) / c.bn);
+        const int64_t waves = (tiles + NUM_CU - 1) / NUM_CU;
+        const double cost = (double)waves * c.bm * c.bn / c.eff;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = {c.bm, c.bn}; }
+    }
+    return best;
+}
+
+template <int IN, int OUT, int TBM, int TBN>
+const void* kernel_for() {
+    if constexpr (IN == IN_F32)
+        return (const void*)gemm32_kernel;
+    else if constexpr (IN == IN_F32X3)
+        return (const void*)gemm32x3_kernel;
+    else
+        return (const void*)gemm16_kernel<IN, OUT, TBM, TBN>;
 }
 
 template <int IN, int OUT>
 int launch(int M, int N, int K, const void* A, int lda, const void* B, int ldb, void* C, int ldc,
-           int64_t ntiles, void* stream) {
-    int tiles_m = (M + BM - 1) / BM;
-    int tiles_n = (N + BN - 1) / BN;
+           void* stream) {
+    const TileChoice t = pick_tile(IN, M, N);
+    int tiles_m = (M + t.bm - 1) / t.bm;
+    int tiles_n = (N + t.bn - 1) / t.bn;
+    const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+    if (ntiles > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
     const char* a = (const char*)A;
     const char* b = (const char*)B;
     char* c = (char*)C;
     void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n};
     const void* fn;
-    if constexpr (IN == IN_F32)
-        fn = (const void*)gemm32_kernel;
-    else if constexpr (IN == IN_F32X3)
-        fn = (const void*)gemm32x3_kernel;
+    if (t.bm == 256)
+        fn = kernel_for<IN, OUT, 256, 256>();
+    else if (t.bm == 192)
+        fn = kernel_for<IN, OUT, 192, 256>();
     else
-        fn = (const void*)gemm16_kernel<IN, OUT>;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)ntiles),
-                                   dim3(NTHREADS), args, 0, (hipStream_t)stream);
+        fn = kernel_for<IN, OUT, 128, 128>();
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)ntiles), dim3(NTHREADS), args, 0,
+                                   (hipStream_t)stream);
     return e == hipSuccess ? DGEMM_OK : DGEMM_ERR_LAUNCH;
 }
 
@@ -874,19 +931,18 @@ int gemm_entry(int M, int N, int K, const void* A, int lda, const void* B, int l
                int ldc, int out, void* stream) {
     if (out != DGEMM_OUT_F32 && out != DGEMM_OUT_SAME) return DGEMM_ERR_INVALID_VALUE;
     const int es_out = out == DGEMM_OUT_F32 ? 4 : in_esize(IN);
-    int64_t ntiles = 0;
-    int st = validate(M, N, K, A, lda, B, ldb, C, ldc, IN, es_out, &ntiles);
+    int st = validate(M, N, K, A, lda, B, ldb, C, ldc, IN, es_out);
     if (st != DGEMM_OK) return st;
     if (M == 0 || N == 0) return DGEMM_OK;
     st = check_device();
     if (st != DGEMM_OK) return st;
-    if (out == DGEMM_OUT_F32) return launch<IN, OUT_F32>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
+    if (out == DGEMM_OUT_F32) return launch<IN, OUT_F32>(M, N, K, A, lda, B, ldb, C, ldc, stream);
     if constexpr (IN == IN_F32 || IN == IN_F32X3)
         return DGEMM_ERR_INVALID_VALUE;  // fp32 inputs always give fp32 C
     else if constexpr (IN == IN_BF16)
-        return launch<IN_BF16, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
+        return launch<IN_BF16, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream);
     else
-        return launch<IN_F16, OUT_F16>(M, N, K, A, lda, B, ldb, C, ldc, ntiles, stream);
+        return launch<IN_F16, OUT_F16>(M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 }  // namespace
@@ -931,12 +987,13 @@ int dgemm_tile_map(int M, int N, int in, int wg, int* tile_rows, int* tile_cols,
                    int* tile_m, int* tile_n) {
     if (M < 0 || N < 0 || (in != IN_F32 && in != IN_BF16 && in != IN_F16 && in != IN_F32X3))
         return DGEMM_ERR_INVALID_VALUE;
-    const int64_t tm_count = ((int64_t)M + BM - 1) / BM;
-    const int64_t tn_count = ((int64_t)N + BN - 1) / BN;
+    const TileChoice t = pick_tile(in, M, N);
+    const int64_t tm_count = ((int64_t)M + t.bm - 1) / t.bm;
+    const int64_t tn_count = ((int64_t)N + t.bn - 1) / t.bn;
     if (tm_count * tn_count > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
     const int nwg = (int)(tm_count * tn_count);
-    if (tile_rows) *tile_rows = BM;
-    if (tile_cols) *tile_cols = BN;
+    if (tile_rows) *tile_rows = t.bm;
+    if (tile_cols) *tile_cols = t.bn;
     if (num_wg) *num_wg = nwg;
     if (wg >= 0 && wg < nwg) {
         int tm = 0, tn = 0;

@@ -128,3 +128,18 @@ def test_tile_map_rejects_bad_arguments():
     z = ctypes.c_int()
     assert lib.dgemm_tile_map(-1, 4, 1, 0, *[ctypes.byref(z)] * 5) == dg.DGEMM_ERR_INVALID_VALUE
     assert lib.dgemm_tile_map(4, 4, 7, 0, *[ctypes.byref(z)] * 5) == dg.DGEMM_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("M,N,fmt,tile", [
+    (4096, 4096, "bf16", (256, 256)),     # 256 tiles: one per CU
+    (16384, 4096, "bf16", (256, 256)),    # four full waves of tiles
+    (4000, 3000, "bf16", (192, 256)),     # 252 tiles instead of 192
+    (4000, 3000, "f16", (192, 256)),
+    (512, 512, "bf16", (128, 128)),       # 16 tiles instead of 4
+    (2048, 2048, "f16", (128, 128)),      # 256 tiles instead of 64
+    (4000, 3000, "f32", (256, 256)),      # fp32 kernels use 256 x 256 only
+    (512, 512, "f32x3", (256, 256)),
+])
+def test_tile_choice(M, N, fmt, tile):
+    info = dg.dgemm_tile_map(M, N, fmt)
+    assert (info["tile_rows"], info["tile_cols"]) == tile

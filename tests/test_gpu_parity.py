@@ -138,6 +138,30 @@ def test_exact_integer_full_size_freivalds(path):
     assert np.array_equal(Cn[rows], C64)
 
 
+@pytest.mark.parametrize("path", ["bf16", "f16"])
+def test_exact_integer_192_tile_freivalds(path):
+    """4000 x 3000 x 4104 selects the 192 x 256 macro-tile: integer inputs,
+    fp32 C, checked everywhere by Freivalds' identity and on sampled rows
+    against the oracle, bit for bit."""
+    M, N, K = 4000, 3000, 4104
+    assert dg.dgemm_tile_map(M, N, path)["tile_rows"] == 192
+    print(f"case freivalds192 {path}", flush=True)
+    A, B = pair(M, N, K, "ints", path, seed=3100)
+    C = run(path, "f32", A, B, a_extra=8, b_extra=8)
+    Cn = to64(C)
+    Aw, Bw = oracle.widen(path, A), oracle.widen(path, B)
+    rng = np.random.default_rng(3101)
+    for _ in range(3):
+        x = rng.integers(-4, 5, N).astype(np.float64)
+        assert np.array_equal(Cn @ x, Aw @ (Bw @ x))
+        y = rng.integers(-4, 5, M).astype(np.float64)
+        assert np.array_equal(y @ Cn, (y @ Aw) @ Bw)
+    rows = sample_rows(M, rng)
+    C64, _ = oracle.gemm(path, A, B, rows=rows)
+    assert np.array_equal(Cn[rows], C64)
+    assert gap_untouched(C)
+
+
 def test_repeat_runs_are_bitwise_identical():
     A, B = pair(1024, 1024, 2048, "normal", "bf16", seed=4000)
     C1 = run("bf16", "f32", A, B)
