@@ -6,10 +6,12 @@ the swizzled layout, the matrix-instruction loop and the epilogue all run inside
 that one kernel) on inputs already resident in HBM.  The headline line is the
 bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
 fp32-input 4096^3 products are measured the same way and reported under
-"per_dtype".
+"per_dtype".  The other parity workloads, and one GPU's row share of the 4096^3
+product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
+the planner splits K, through gemm_ex with a workspace.
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
-                    [--no-cpu-baseline] [--no-per-dtype]
+                    [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -34,7 +36,10 @@ DESCRIPTION = {
     "f16_4096": "fp16 GEMM M=N=K=4096, row-major A and B, uniform[-1,1] inputs, fp32 accumulate, fp16 C",
     "f32_4096": "fp32 GEMM M=N=K=4096, row-major A and B, uniform[-1,1] inputs, fp32 accumulate, fp32 C",
 }
-KERNEL_SOURCE = os.path.join(ROOT, "dense_gemm_matrix_amd", "csrc", "dgemm.hip")
+# The files that define the dominant (16-bit) kernel: counters taken on it stay
+# valid while these are unchanged.
+KERNEL_SOURCES = [os.path.join(ROOT, "dense_gemm_matrix_amd", "csrc", f)
+                  for f in ("gemm16.hip", "kern_common.h", "dgemm_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -48,8 +53,11 @@ def tflops(M: int, N: int, K: int, seconds: float) -> float:
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -134,6 +142,54 @@ def copy_calibration(gib: float = 1.0, reps: int = 5):
                       "reps": reps}), flush=True)
 
 
+# (label, workload name or (dtype, M, N, K), path)
+SHAPES = [("f32 512^3", "f32_512", "f32"),
+          ("bf16 16384x4096x4096, bf16 C", "bf16_16384x4096x4096", "bf16"),
+          ("bf16 4000x3000x4104, bf16 C", "bf16_4000x3000x4104", "bf16"),
+          ("bf16 512x4096x4096 (row share of 4096^3 over 8 GPUs), bf16 C",
+           ("bf16", 512, 4096, 4096), "bf16")]
+
+
+def other_shapes(dg, args):
+    """Per shape: the plain entry point, and gemm_ex with the workspace its
+    split-K plan asks for when the plan splits."""
+    import torch
+    from synth_inputs import pair, to_torch, torch_dtype
+    out = []
+    for label, wl, path in SHAPES:
+        if isinstance(wl, str):
+            A, B, Ad, Bd, Cd, meta = device_inputs(wl)
+            M, N, K = meta["M"], meta["N"], meta["K"]
+        else:
+            dt, M, N, K = wl
+            A, B = pair(M, N, K, "normal002", dt, seed=6000)
+            Ad, Bd = to_torch(A, dt).to("cuda"), to_torch(B, dt).to("cuda")
+            Cd = torch.empty((M, N), dtype=torch_dtype(dt), device="cuda")
+        print(f"bench: shape {label}", file=sys.stderr, flush=True)
+        plain = {"f32": dg.gemm_f32, "bf16": dg.gemm_bf16, "f16": dg.gemm_f16}[path]
+        flop_s = gemm_flops(M, N, K)
+        steps = max(10, min(args.steps, int(2e4 * 1e9 / flop_s)))
+        warm = max(3, min(args.warmup, steps))
+        t, _ = time_gemm(plain, Ad, Bd, Cd, steps, warm)
+        rec = {"shape": label, "M": M, "N": N, "K": K, "steps": steps,
+               "plain_us": round(t * 1e6, 2), "plain_tflops": round(tflops(M, N, K, t), 2)}
+        plan = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(Cd.dtype == Ad.dtype and
+                                                                   path != "f32"))
+        rec["plan"] = plan
+        if plan["splits"] > 1:
+            ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+
+            def split_entry(a, b, c, stream=None, ws=ws):
+                dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
+            t2, _ = time_gemm(split_entry, Ad, Bd, Cd, steps, warm)
+            rec["split_us"] = round(t2 * 1e6, 2)
+            rec["split_tflops"] = round(tflops(M, N, K, t2), 2)
+            del ws
+        out.append(rec)
+        del Ad, Bd, Cd
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +198,7 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-dtype", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -207,6 +264,8 @@ def main():
                         "frac_of_peak": round(v2 / peak, 4), "peak": round(peak, 1)}
             del a2, b2, c2
         line["per_dtype"] = per
+    if not args.no_shapes:
+        line["other_shapes"] = other_shapes(dg, args)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)

@@ -32,6 +32,14 @@ _lib.dgemm_status_string.restype = ctypes.c_char_p
 _P = ctypes.POINTER(ctypes.c_int)
 _lib.dgemm_tile_map.argtypes = [_c_int, _c_int, _c_int, _c_int, _P, _P, _P, _P, _P]
 _lib.dgemm_tile_map.restype = _c_int
+_c_float, _c_size_t = ctypes.c_float, ctypes.c_size_t
+_lib.gemm_ex.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
+                         _c_int, _c_void_p, _c_int, _c_float, _c_float, _c_void_p, _c_int,
+                         _c_void_p, _c_size_t, _c_void_p]
+_lib.gemm_ex.restype = _c_int
+_lib.gemm_ex_plan.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_size_t, _P, _P, _P,
+                              ctypes.POINTER(_c_size_t)]
+_lib.gemm_ex_plan.restype = _c_int
 
 DGEMM_OK = 0
 DGEMM_ERR_INVALID_VALUE = 1
@@ -43,7 +51,10 @@ DGEMM_ERR_DEVICE = 6
 DGEMM_ERR_LAUNCH = 7
 DGEMM_OUT_F32 = 0
 DGEMM_OUT_SAME = 1
+DGEMM_ACT_NONE = 0
+DGEMM_ACT_RELU = 1
 IN_CODES = {"f32": 0, "bf16": 1, "f16": 2, "f32x3": 3}
+_TORCH_IN = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
 
 
 class DgemmError(RuntimeError):
@@ -138,15 +149,74 @@ def gemm_f16(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> 
     _gemm16(_lib.gemm_f16, torch.float16, A, B, C, stream)
 
 
-_ENTRY = {torch.float32: gemm_f32, torch.bfloat16: gemm_bf16, torch.float16: gemm_f16}
+def gemm_ex_plan(in_fmt: str, M: int, N: int, K: int, workspace_bytes: int,
+                 out_same: bool = False) -> dict:
+    """Host query of the plan gemm_ex uses with `workspace_bytes` available."""
+    v = [ctypes.c_int(-1) for _ in range(3)]
+    used = _c_size_t(0)
+    out = DGEMM_OUT_SAME if out_same else DGEMM_OUT_F32
+    _check(_lib.gemm_ex_plan(IN_CODES[in_fmt], out, M, N, K, int(workspace_bytes),
+                             *[ctypes.byref(x) for x in v], ctypes.byref(used)))
+    return {"tile_rows": v[0].value, "tile_cols": v[1].value, "splits": v[2].value,
+            "workspace_bytes": used.value}
 
 
-def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, stream=None) -> torch.Tensor:
-    """Allocates C (torch allocator) and computes C = A @ B with the library."""
+def gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float = 1.0,
+            beta: float = 0.0, bias: torch.Tensor = None, relu: bool = False,
+            workspace: torch.Tensor = None, in_fmt: str = None, stream=None) -> None:
+    """C = act(alpha * A @ B + beta * C + bias) through the library's gemm_ex.
+
+    `workspace` (a device tensor, any dtype) lends scratch memory for a split-K
+    plan; None means no split.  `in_fmt` picks "f32x3" for fp32 data on the
+    3 x bf16 path; by default it follows A's dtype."""
+    M, N, K = _shapes(A, B, C)
+    fmt = in_fmt or _TORCH_IN.get(A.dtype)
+    if fmt is None or B.dtype != A.dtype or (fmt == "f32x3" and A.dtype != torch.float32):
+        raise TypeError("unsupported input dtypes")
+    if C.dtype == torch.float32:
+        out = DGEMM_OUT_F32
+    elif C.dtype == A.dtype:
+        out = DGEMM_OUT_SAME
+    else:
+        raise TypeError("C must be float32 or the input dtype")
+    bias_ptr = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 1 or bias.numel() != N \
+                or not bias.is_contiguous() or bias.device != C.device:
+            raise ValueError("bias must be a contiguous float32 device vector of length N")
+        bias_ptr = bias.data_ptr()
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != C.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on C's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(C.device):
+        _check(_lib.gemm_ex(IN_CODES[fmt], out, M, N, K, A.data_ptr(), _pitch(A, K),
+                            B.data_ptr(), _pitch(B, N), C.data_ptr(), _pitch(C, N),
+                            float(alpha), float(beta), bias_ptr,
+                            DGEMM_ACT_RELU if relu else DGEMM_ACT_NONE, ws_ptr, ws_bytes,
+                            _stream(C, stream)))
+
+
+def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, *, bias: torch.Tensor = None,
+           relu: bool = False, alpha: float = 1.0, split_k: bool = True,
+           stream=None) -> torch.Tensor:
+    """Allocates C (torch allocator) and computes C = act(alpha * A @ B + bias).
+
+    With split_k, the workspace a split-K plan asks for is taken from torch's
+    allocator on the same stream (it is free again once the kernels that use it
+    have run, in stream order)."""
     if out_dtype is None:
         out_dtype = A.dtype
     C = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype, device=A.device)
-    _ENTRY[A.dtype](A, B, C, stream)
+    ws = None
+    if split_k:
+        fmt = _TORCH_IN[A.dtype]
+        plan = gemm_ex_plan(fmt, A.shape[0], B.shape[1], A.shape[1], 1 << 40,
+                            out_same=(out_dtype == A.dtype and fmt != "f32"))
+        if plan["splits"] > 1:
+            ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=A.device)
+    gemm_ex(A, B, C, alpha=alpha, bias=bias, relu=relu, workspace=ws, stream=stream)
     return C
 
 

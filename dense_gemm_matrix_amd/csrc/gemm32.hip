@@ -1,0 +1,437 @@
+// gemm32.hip -- GEMM kernels for fp32 inputs on gfx950 (MI355X).
+//
+//   * gemm32_kernel: gfx950 has no reduced-precision (xf32) matrix
+//     instruction, so products use full-precision v_mfma_f32_32x32x2_f32.
+//     Operands are staged through registers (B's 8 x 4 fp32 blocks are
+//     transposed by register renaming), double-buffered in LDS with BK = 32.
+//   * gemm32x3_kernel: the same data on bf16 matrix instructions, each input
+//     split in two bf16 parts and three products taken per term.
+//
+// Workgroup layout, tile map, swizzle principle, edge handling and epilogue as
+// in the 16-bit kernel: 256 x 256 macro-tile, 4 waves in a 2 x 2 layout, each
+// wave 128 x 128 as 4 x 4 blocks of 32 x 32 fp32 accumulators.
+
+#include "kern_common.h"
+
+namespace dgemm {
+namespace {
+
+constexpr int BM = 256;                       // macro-tile rows
+constexpr int BN = 256;                       // macro-tile columns
+constexpr int BK = 32;                        // K per step (fp32: 128-byte LDS rows)
+
+// Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
+// and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when
+// unsplit).  Shifts the operand bases and narrows K to the window.
+__device__ __forceinline__ void split_k_window(const char* __restrict__& A,
+                                               const char* __restrict__& B,
+                                               char* __restrict__& C, int& K,
+                                               int ldb, int kchunk, int64_t c_zstride) {
+    const int z = (int)blockIdx.y;
+    const int kbeg = z * kchunk;
+    A += (int64_t)kbeg * 4;
+    B += (int64_t)kbeg * ldb * 4;
+    C += z * c_zstride;
+    K = (K - kbeg) < kchunk ? (K - kbeg) : kchunk;
+}
+
+constexpr int ROW_CHUNKS32 = 8;                  // 16-byte chunks per staged row (32 fp32)
+constexpr int STAGE_CHUNKS32 = BM * ROW_CHUNKS32;  // one operand's stage: 32 KiB
+
+// LDS slot of chunk c in staged row r.  With phi(r) = (r ^ (r >> 3)) & 7, the 8
+// consecutive rows an operand read touches get 8 distinct slots, and so do the
+// 8 aligned rows of any 16-row group with equal parity.
+__device__ __forceinline__ int lds32_index(int row, int chunk) {
+    return row * ROW_CHUNKS32 + (chunk ^ ((row ^ (row >> 3)) & 7));
+}
+
+// Zero the fp32 elements of a chunk at and after `valid` (valid <= 0: all).
+__device__ __forceinline__ u32x4 mask_tail32(u32x4 v, int valid) {
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = (d < valid) ? (uint32_t)v[d] : 0u;
+    return out;
+}
+
+template <bool EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
+    int kchunk, int64_t c_zstride, EpiArgs epi) {
+    split_k_window(A, B, C, K, ldb, kchunk, c_zstride);
+    // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x 32 KiB.  Both operands are
+    // stored K-contiguous: B is transposed on its way through registers.
+    __shared__ u32x4 lds[2][2][STAGE_CHUNKS32];
+
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int nk = (K + BK - 1) / BK;
+    const bool ragged_k = (K % BK) != 0;
+
+    // A staging: thread -> chunk ac of rows ar0 + 32 i, i = 0..7.
+    const int ac = tid & 7;
+    const int ar0 = tid >> 3;
+    // B staging: thread -> a block of 8 K-rows (kb) by 4 columns (nb).
+    const int kb = tid & 3;
+    const int nb = tid >> 2;
+
+    int voff_a[8], voff_b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        voff_a[i] = (ar0 + 32 * i) * lda * 4 + ac * 16;
+        voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
+    }
+
+    u32x4 ra[8], rb[8];
+
+    auto load_step = [&](int kt, bool tail) {
+        const int k0 = kt * BK;
+        const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
+        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
+        const int rows_b = (K - k0) < BK ? (K - k0) : BK;
+        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
+        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ra[i] = load16(rsa, voff_a[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        if (tail) {
+            // Columns of A at or past K hold other data (row padding or the next
+            // row); they must be exact zeros, since the matching B rows are.
+            const int valid = K - k0 - ac * 4;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ra[i] = mask_tail32(ra[i], valid);
+        }
+    };
+
+    auto store_step = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lds[s][0][lds32_index(ar0 + 32 * i, ac)] = ra[i];
+        // 8 K-rows x 4 columns -> 4 columns x two chunks of 4 K values.
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
+                lds[s][1][lds32_index(nb * 4 + cc, kb * 2 + h)] = v;
+            }
+        }
+    };
+
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int g = lane >> 5;   // lane group: which chunk of a chunk pair
+    const int li = lane & 31;  // row of A / column of B within a 32-block
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    // Operand fragments for one chunk pair (8 k): lane group g reads chunk
+    // 2 * kp + g of its 4 A rows and 4 B columns.  Two register sets alternate
+    // so that the reads for pair kp + 1 are in flight while kp computes.
+    u32x4 fa[2][4], fb[2][4];
+
+    auto read_frags = [&](int s, int kp, u32x4 (&a)[4], u32x4 (&b)[4]) {
+        const int ch = 2 * kp + g;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) a[mi] = lds[s][0][lds32_index(wm * 128 + mi * 32 + li, ch)];
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) b[nj] = lds[s][1][lds32_index(wn * 128 + nj * 32 + li, ch)];
+    };
+
+    auto mfma_frags = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        as_float(a[mi][e]), as_float(b[nj][e]), acc[mi][nj], 0, 0, 0);
+    };
+
+    // Schedule of one K step (stage `cur` in LDS, stage cur ^ 1 being filled):
+    // global loads for step kt + 1 -> registers; pairs 0, 1, 2: read the next
+    // pair's fragments, then compute; registers -> LDS stage cur ^ 1; barrier;
+    // read pair 0 of stage cur ^ 1, then compute pair 3 (already in registers),
+    // which covers that read's latency.  sched_barrier keeps the compiler from
+    // sinking the fragment reads down to their uses.
+    if (nk > 0) {
+        load_step(0, ragged_k && nk == 1);
+        store_step(0);
+        __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
+            read_frags(cur, 1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 2, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 3, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) store_step(cur ^ 1);
+            __syncthreads();
+            if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi);
+}
+
+// ---------------------------------------------------------------- fp32 via 3 x bf16
+
+// fp32 inputs split into two bf16 parts, x = hi + lo + e with hi = bf16(x),
+// lo = bf16(x - hi) (both round to nearest even; x - hi is exact in fp32), so
+// |e| <= 2^-16 |x|.  a * b is taken as ah*bh + ah*bl + al*bh: the dropped
+// al*bl and the two truncations leave a relative error of at most about
+// 3 * 2^-16 per product, before fp32 accumulation.  Three bf16 MFMAs per
+// product at 8x the fp32 MFMA rate.
+//
+// Operands are staged through registers: each thread loads fp32 pieces of A
+// (8 consecutive k of one row) and B (an 8 k x 4 column block), splits them,
+// and writes hi and lo parts to LDS as K-contiguous bf16 rows (B is transposed
+// on the way, by its choice of which values to pack), so both operands are
+// read with ds_read_b128.  Double-buffered LDS, BK = 32.
+
+constexpr int X3_ROW = BK * 2;                  // 64-byte bf16 rows: 4 chunks
+constexpr int X3_PART = BM * X3_ROW;            // one part of one operand: 16 KiB
+constexpr int X3_STAGE = 4 * X3_PART;           // A hi, A lo, B hi, B lo: 64 KiB
+
+__device__ __forceinline__ int x3_off(int row, int chunk) {
+    return row * X3_ROW + ((chunk ^ ((row ^ (row >> 2)) & 3)) << 4);
+}
+
+// Split 8 fp32 values into packed hi and lo bf16 parts (element i in the low
+// half of word i / 2 when i is even).
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const __bf16 h0 = (__bf16)x[2 * w], h1 = (__bf16)x[2 * w + 1];
+        const __bf16 l0 = (__bf16)(x[2 * w] - (float)h0);
+        const __bf16 l1 = (__bf16)(x[2 * w + 1] - (float)h1);
+        hi[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo[w] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+}
+
+template <bool EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
+    int kchunk, int64_t c_zstride, EpiArgs epi) {
+    split_k_window(A, B, C, K, ldb, kchunk, c_zstride);
+    __shared__ __attribute__((aligned(1024))) char smem[2 * X3_STAGE];
+
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int nk = (K + BK - 1) / BK;
+    const bool ragged_k = (K % BK) != 0;
+
+    // A staging: thread -> 8 consecutive k (two 16-byte fp32 pieces) of rows
+    // ar0 + 64 i, i = 0..3, k chunk ac.
+    const int ac = tid & 3;
+    const int ar0 = tid >> 2;
+    // B staging: thread -> an 8 k x 4 column block (k rows 8 kb .., columns 4 nb ..).
+    const int kb = tid & 3;
+    const int nb = tid >> 2;
+
+    int voff_a[4], voff_b[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff_a[i] = (ar0 + 64 * i) * lda * 4 + ac * 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
+
+    u32x4 ra[8], rb[8];
+
+    auto load_step = [&](int kt, bool tail) {
+        const int k0 = kt * BK;
+        const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
+        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
+        const int rows_b = (K - k0) < BK ? (K - k0) : BK;
+        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
+        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ra[2 * i] = load16(rsa, voff_a[i]);
+            ra[2 * i + 1] = load16(rsa, voff_a[i] + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        if (tail) {
+            // Columns of A at or past K hold other data (row padding or the next
+            // row); they must be exact zeros, since the matching B rows are.
+            const int valid = K - k0 - ac * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[2 * i] = mask_tail32(ra[2 * i], valid);
+                ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
+            }
+        }
+    };
+
+    auto store_step = [&](int s) {
+        char* st = smem + s * X3_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = as_float(ra[2 * i][e]);
+                x[4 + e] = as_float(ra[2 * i + 1][e]);
+            }
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            const int off = x3_off(ar0 + 64 * i, ac);
+            *(u32x4*)(st + off) = hi;
+            *(u32x4*)(st + X3_PART + off) = lo;
+        }
+        // B: column cc of the block, 8 consecutive k -> one chunk per part.
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = as_float(rb[e][cc]);
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            const int off = x3_off(nb * 4 + cc, kb);
+            *(u32x4*)(st + 2 * X3_PART + off) = hi;
+            *(u32x4*)(st + 3 * X3_PART + off) = lo;
+        }
+    };
+
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    // Fragments of one 16-k chunk pair: [part][block], part 0 = hi, 1 = lo.
+    u32x4 fa[2][2][4], fb[2][2][4];
+
+    auto read_frags = [&](int s, int kp, u32x4 (&a)[2][4], u32x4 (&b)[2][4]) {
+        const char* st = smem + s * X3_STAGE;
+        const int ch = 2 * kp + g;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                a[p][mi] = *(const u32x4*)(st + p * X3_PART + x3_off(wm * 128 + mi * 32 + li, ch));
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                b[p][nj] = *(const u32x4*)(st + (2 + p) * X3_PART + x3_off(wn * 128 + nj * 32 + li, ch));
+        }
+    };
+
+    auto mfma_frags = [&](const u32x4 (&a)[2][4], const u32x4 (&b)[2][4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj) {
+                // small terms first, then the leading one
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[1][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[1][nj]), acc[mi][nj], 0, 0, 0);
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
+            }
+        }
+    };
+
+    // Per step: global loads of step kt + 1 -> registers; read pair 1 while
+    // pair 0 computes; split and write step kt + 1 to the other stage;
+    // barrier; read pair 0 of step kt + 1 while pair 1 computes.
+    if (nk > 0) {
+        load_step(0, ragged_k && nk == 1);
+        store_step(0);
+        __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
+            read_frags(cur, 1, fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) store_step(cur ^ 1);
+            __syncthreads();
+            if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frags(fa[1], fb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi);
+}
+
+hipError_t go(const void* fn, const GemmLaunch& L) {
+    const char* a = L.A;
+    const char* b = L.B;
+    char* c = L.C;
+    int M = L.M, N = L.N, K = L.K, lda = L.lda, ldb = L.ldb, ldc = L.ldc;
+    int tiles_m = L.tiles_m, tiles_n = L.tiles_n, kchunk = L.kchunk;
+    int64_t zs = L.c_zstride;
+    EpiArgs e = L.e;
+    void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &kchunk, &zs, &e};
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits),
+                           dim3(NTHREADS), args, 0, L.stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm32(const GemmLaunch& L) {
+    if (L.out != OUT_F32 || L.tbm != BM || L.tbn != BN) return hipErrorInvalidValue;
+    if (L.in == IN_F32)
+        return go(L.epi ? (const void*)gemm32_kernel<true> : (const void*)gemm32_kernel<false>, L);
+    if (L.in == IN_F32X3)
+        return go(L.epi ? (const void*)gemm32x3_kernel<true> : (const void*)gemm32x3_kernel<false>,
+                  L);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dgemm

@@ -11,15 +11,16 @@
  * A is row-major M x K with row pitch lda elements, B is row-major K x N with
  * row pitch ldb, C is row-major M x N with row pitch ldc.  Products are
  * accumulated in fp32 (the pages' matrix instructions all accumulate in fp32).
- * C is overwritten; there is no alpha/beta.  Elements of C outside the M x N
+ * C is overwritten (gemm_ex adds alpha, beta, bias and ReLU).  Elements of C outside the M x N
  * window (the ldc - N gap of each row) are never written.
  *
- * Ownership: A, B and C are DEVICE pointers owned by the caller.  The library
- * allocates no device memory and keeps no pointer after a call returns.
+ * Ownership: A, B and C (and gemm_ex's bias and workspace) are DEVICE pointers
+ * owned by the caller.  The library allocates no device memory and keeps no
+ * pointer after a call returns.
  *
- * Execution: each call validates its arguments, enqueues one kernel on
- * `stream` (a hipStream_t; NULL means the default stream) and returns without
- * waiting.  Results are visible once the stream has synchronised.  Calls from
+ * Execution: each call validates its arguments, enqueues its kernels (one,
+ * or two for a split-K plan of gemm_ex) on `stream` (a hipStream_t; NULL
+ * means the default stream) and returns without waiting.  Results are visible once the stream has synchronised.  Calls from
  * different host threads on different streams are independent.
  *
  * Errors: a non-zero status is returned and NOTHING is enqueued when the
@@ -39,17 +40,20 @@
 #ifndef DGEMM_H
 #define DGEMM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
 typedef enum {
     DGEMM_OK = 0,
-    DGEMM_ERR_INVALID_VALUE = 1, /* negative M/N/K, NULL pointer with nonzero extent, bad `out` */
+    DGEMM_ERR_INVALID_VALUE = 1, /* negative M/N/K, NULL pointer with nonzero extent, bad enum   */
     DGEMM_ERR_LEADING_DIM = 2,   /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N)           */
-    DGEMM_ERR_MISALIGNED = 3,    /* a base pointer or a row pitch in bytes not a multiple of 16   */
-    DGEMM_ERR_ALIAS = 4,         /* C's byte range overlaps A's or B's                           */
-    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 32*ldb*esize bytes reach 2 GiB (32-bit offsets) */
+    DGEMM_ERR_MISALIGNED = 3,    /* a base pointer or a row pitch in bytes not a multiple of 16
+                                    (bias: of 4)                                               */
+    DGEMM_ERR_ALIAS = 4,         /* C overlaps A, B or the bias; the workspace overlaps any of them */
+    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 128*ldb bytes reach 2 GiB (32-bit offsets)  */
     DGEMM_ERR_DEVICE = 6,        /* no current device, or it is not a gfx950                     */
     DGEMM_ERR_LAUNCH = 7         /* the kernel launch reported an error                          */
 } dgemm_status;
@@ -109,14 +113,80 @@ int gemm_f16(int M, int N, int K,
              int out,
              void* stream);
 
+/* Input format codes of gemm_ex, gemm_ex_plan and dgemm_tile_map. */
+typedef enum {
+    DGEMM_IN_F32 = 0,        /* fp32, full-fp32 matrix instruction (as gemm_f32)     */
+    DGEMM_IN_BF16 = 1,       /* bf16 storage (as gemm_bf16)                           */
+    DGEMM_IN_F16 = 2,        /* fp16 storage (as gemm_f16)                            */
+    DGEMM_IN_F32_3XBF16 = 3  /* fp32 through the 3 x bf16 split (as gemm_f32_3xbf16) */
+} dgemm_in;
+
+/* Activation of gemm_ex's epilogue. */
+typedef enum {
+    DGEMM_ACT_NONE = 0,
+    DGEMM_ACT_RELU = 1  /* x < 0 -> 0; NaN passes through */
+} dgemm_act;
+
+/*
+ * The general entry point: GEMM with a fused epilogue and an optional split-K
+ * plan.
+ *
+ *     C[i][j] := act(alpha * sum_k A[i][k] * B[k][j] + beta * C[i][j] + bias[j])
+ *
+ * The epilogue is evaluated in fp32 on the fp32 sum and rounded once (to
+ * nearest even) to C's format; the old C is read in C's format and only when
+ * beta != 0 (so C may hold NaN when beta == 0, as in BLAS).  bias is NULL or
+ * a device array of N fp32 values (4-byte aligned).  With alpha = 1, beta = 0,
+ * bias = NULL and act = DGEMM_ACT_NONE this is exactly the plain entry point
+ * for `in`.  The hgemm page's closing discussion names the library kernel it
+ * measures against, a bf16 GEMM with a fused ReLU epilogue; bias and
+ * alpha/beta are the usual companions of that epilogue.
+ *
+ * Split-K (the nine-levels tutorial, section 2.9: K divided into pieces that
+ * separate workgroups reduce, joined by a second reduction pass): when the
+ * grid of output tiles cannot fill the GPU's 256 CUs (few or thin tiles, deep
+ * K), a plan may split K into s pieces.  The GEMM kernel then writes s fp32
+ * partial products into `workspace` and a second kernel sums them in a fixed
+ * order (ascending piece), applies the epilogue and writes C; results are
+ * deterministic for a given (shape, workspace_bytes) and differ from the
+ * unsplit plan's only in fp32 summation order.  A split plan is used only if
+ * the caller's workspace (device memory, 16-byte aligned, at least
+ * workspace_bytes long, not overlapping A, B, C or bias) holds it; with
+ * workspace = NULL / workspace_bytes = 0 the call never splits.  The
+ * workspace is scratch: its contents before and after the call are
+ * unspecified, and calls that share one workspace must be ordered (same
+ * stream).  gemm_ex_plan reports the plan and the bytes it uses.
+ *
+ * in:  a dgemm_in code.  out: DGEMM_OUT_F32, or DGEMM_OUT_SAME for C in the
+ * input format (for fp32 inputs both mean fp32).  Other arguments,
+ * preconditions and errors as the plain entry points.
+ */
+int gemm_ex(int in, int out, int M, int N, int K,
+            const void* A, int lda,
+            const void* B, int ldb,
+            void* C, int ldc,
+            float alpha, float beta, const float* bias, int act,
+            void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/*
+ * Host-side query of the plan gemm_ex would use with `workspace_bytes`
+ * available (no GPU needed): macro-tile shape, split count (1 = unsplit) and
+ * the workspace bytes that plan uses (0 when unsplit).  Any output pointer
+ * may be NULL.  Returns DGEMM_OK, or DGEMM_ERR_INVALID_VALUE for negative
+ * sizes or a bad `in` / `out`.
+ */
+int gemm_ex_plan(int in, int out, int M, int N, int K, size_t workspace_bytes,
+                 int* tile_rows, int* tile_cols, int* splits, size_t* workspace_used);
+
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* dgemm_status_string(int status);
 
 /*
  * Host-side query of the kernel's work distribution, for tests and tuning; it
  * launches nothing and needs no GPU.  For a problem of M x N outputs and input
- * format `in` (0 = fp32, 1 = bf16, 2 = fp16, 3 = fp32 via 3 x bf16), writes the
- * macro-tile shape and
+ * format `in` (a dgemm_in code), as the plain entry points launch it (no
+ * split), writes the macro-tile shape and
  * the number of workgroups, and, when wg is in [0, *num_wg), the output tile
  * (row block *tile_m, column block *tile_n) that workgroup `wg` computes.  The
  * mapping is a bijection from workgroups to tiles: it first gives each of the

@@ -17,7 +17,8 @@ import os
 
 import numpy as np
 
-from .parity import U_OUT, bound, check  # noqa: F401  (re-exported)
+from .epilogue import epilogue  # noqa: F401  (re-exported)
+from .parity import U_OUT, bound, bound_epilogue, check  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")

@@ -18,6 +18,15 @@ Derivation: an fp32 accumulator s of exact products satisfies |s - C64| <= tol*S
 rounding s once to the output adds at most u_out*|s| <= u_out*(|C64| + tol*S),
 plus sub_out if the result lands in the subnormal range.
 NaN or Inf in C_gpu always fails (all workloads here are finite).
+
+With the fused epilogue E = act(alpha*C64 + beta*C_old + bias) the GPU scales
+its fp32 sum, adds the two other terms in fp32 and rounds once.  The sum's error
+becomes |alpha|*tol*S; the fp32 multiply and two adds (or fused multiply-adds)
+add at most 2^-22 * T with T = |alpha*C64| + |beta*C_old| + |bias| (a generous
+count of 4 roundings of 2^-24 each); ReLU is 1-Lipschitz and cannot enlarge an
+error; rounding to the output adds u_out*|E|:
+
+    |C_gpu - E| <= (|alpha|*tol*S + 2^-22 * T) * (1 + u_out) + u_out*|E| + sub_out
 """
 import numpy as np
 
@@ -32,18 +41,27 @@ def bound(C64: np.ndarray, S: np.ndarray, tol: float, out: str) -> np.ndarray:
     return tol * S * (1.0 + u) + u * np.abs(C64) + SUB_OUT[out]
 
 
+def bound_epilogue(E: np.ndarray, T: np.ndarray, S: np.ndarray, alpha: float, tol: float,
+                   out: str) -> np.ndarray:
+    u = U_OUT[out]
+    pre = tol * abs(alpha) * S + 2.0 ** -22 * T
+    return pre * (1.0 + u) + u * np.abs(E) + SUB_OUT[out]
+
+
 def check(C_gpu: np.ndarray, C64: np.ndarray, S: np.ndarray, tol: float, out: str,
-          C_round=None) -> dict:
+          C_round=None, b: np.ndarray = None) -> dict:
     """Elementwise check.  C_gpu is the GPU result already widened to float64.
 
-    Returns ok, n_bad, max_ratio (max error / bound), the first failing index,
-    and, when C_round (the oracle's direct rounding, widened) is given, the
-    fraction of elements equal to it.
+    C64 is the reference value (for an epilogue, E) and b the bound (default:
+    bound(C64, S, tol, out)).  Returns ok, n_bad, max_ratio (max error /
+    bound), the first failing index, and, when C_round (the oracle's direct
+    rounding, widened) is given, the fraction of elements equal to it.
     """
     C_gpu = np.asarray(C_gpu, dtype=np.float64)
     if C_gpu.shape != C64.shape:
         raise ValueError(f"shape {C_gpu.shape} != oracle {C64.shape}")
-    b = bound(C64, S, tol, out)
+    if b is None:
+        b = bound(C64, S, tol, out)
     err = np.abs(C_gpu - C64)
     finite = np.isfinite(C_gpu)
     bad = ~finite | ~(err <= b)

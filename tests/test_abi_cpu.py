@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16", "dgemm_status_string",
-                 "dgemm_tile_map"):
+    for want in ("gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16", "gemm_ex",
+                 "gemm_ex_plan", "dgemm_status_string", "dgemm_tile_map"):
         assert want in names
 
 
@@ -85,8 +85,9 @@ def test_validation_errors(fn):
     # 32-bit descriptor range
     huge = (1 << 31) // (256 * es)
     assert call(fn, 8, 8, 8, PA, huge, PB, ok_ld, PC, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+    # one K step of B spans 128 * ldb bytes (64 rows of 16-bit data, 32 of fp32)
     far = 0x7000000000
-    assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // (32 * es), far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // 128, far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
 
 
 
@@ -143,3 +144,84 @@ def test_tile_map_rejects_bad_arguments():
 def test_tile_choice(M, N, fmt, tile):
     info = dg.dgemm_tile_map(M, N, fmt)
     assert (info["tile_rows"], info["tile_cols"]) == tile
+
+
+# ---------------------------------------------------------------- gemm_ex
+
+def call_ex(in_fmt, out, M, N, K, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=0, act=0,
+            ws=0, ws_bytes=0):
+    return dg.raw().gemm_ex(in_fmt, out, M, N, K, V(A), lda, V(B), ldb, V(C), ldc, alpha, beta,
+                            V(bias) if bias else None, act, V(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("in_fmt", [0, 1, 2, 3])
+def test_gemm_ex_validation_errors(in_fmt):
+    es = 4 if in_fmt in (0, 3) else 2
+    ld = 64
+    ok = dict(A=PA, lda=ld, B=PB, ldb=ld, C=PC, ldc=ld)
+    INV, MIS, ALI = dg.DGEMM_ERR_INVALID_VALUE, dg.DGEMM_ERR_MISALIGNED, dg.DGEMM_ERR_ALIAS
+    assert dg.raw().gemm_ex(7, 0, 8, 8, 8, V(PA), ld, V(PB), ld, V(PC), ld, 1.0, 0.0, None, 0,
+                            None, 0, None) == INV
+    assert call_ex(in_fmt, 2, 8, 8, 8, **ok) == INV          # bad out
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, act=2) == INV   # bad act
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, ws=0, ws_bytes=64) == INV  # bytes without memory
+    assert call_ex(in_fmt, 0, -1, 8, 8, **ok) == INV
+    assert call_ex(in_fmt, 0, 8, 8, 72, **ok) == dg.DGEMM_ERR_LEADING_DIM
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, bias=0x40000002) == MIS
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, ws=0x50000008, ws_bytes=1 << 20) == MIS
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, bias=PC + 4 * 8) == ALI   # bias inside C
+    assert call_ex(in_fmt, 0, 8, 8, 8, A=PA, lda=ld, B=PB, ldb=ld, C=PA, ldc=ld) == ALI
+    # a workspace that a split plan would use, overlapping A
+    M, N, K = 64, 64, 1 << 14
+    plan = dg.gemm_ex_plan({0: "f32", 1: "bf16", 2: "f16", 3: "f32x3"}[in_fmt], M, N, K, 1 << 30)
+    assert plan["splits"] > 1
+    assert call_ex(in_fmt, 0, M, N, K, A=PA, lda=K, B=PB, ldb=N, C=PC, ldc=N,
+                   ws=PA + 16 * es, ws_bytes=1 << 30) == ALI
+    # empty outputs stay a no-op without a device, whatever the epilogue
+    assert call_ex(in_fmt, 0, 0, 8, 8, 0, 8, 0, 8, 0, 8, alpha=2.0, beta=1.0, act=1) == dg.DGEMM_OK
+
+
+def test_gemm_ex_plan_rejects_bad_arguments():
+    lib = dg.raw()
+    z = ctypes.c_int()
+    u = ctypes.c_size_t()
+    assert lib.gemm_ex_plan(5, 0, 8, 8, 8, 0, *[ctypes.byref(z)] * 3, ctypes.byref(u)) == \
+        dg.DGEMM_ERR_INVALID_VALUE
+    assert lib.gemm_ex_plan(1, 3, 8, 8, 8, 0, *[ctypes.byref(z)] * 3, ctypes.byref(u)) == \
+        dg.DGEMM_ERR_INVALID_VALUE
+    assert lib.gemm_ex_plan(1, 0, 8, -8, 8, 0, *[ctypes.byref(z)] * 3, ctypes.byref(u)) == \
+        dg.DGEMM_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("M,N,K,fmt", [(4096, 4096, 4096, "bf16"), (16384, 4096, 4096, "bf16"),
+                                       (4000, 3000, 4104, "bf16"), (4096, 4096, 4096, "f32"),
+                                       (512, 4096, 4096, "bf16"), (512, 512, 512, "f32")])
+def test_plan_without_workspace_is_the_plain_launch(M, N, K, fmt):
+    p = dg.gemm_ex_plan(fmt, M, N, K, 0)
+    t = dg.dgemm_tile_map(M, N, fmt)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    assert (p["tile_rows"], p["tile_cols"]) == (t["tile_rows"], t["tile_cols"])
+
+
+@pytest.mark.parametrize("M,N,K,fmt,splits", [
+    (4096, 4096, 4096, "bf16", 1),      # 256 tiles already fill the CUs
+    (16384, 4096, 4096, "bf16", 1),
+    (4000, 3000, 4104, "bf16", 1),
+    (512, 4096, 4096, "bf16", None),    # one GPU's row share of the 4096^3 problem
+    (512, 512, 512, "f32", None),       # 4 tiles of 256^2
+    (64, 64, 4096, "f16", None),
+    (256, 256, 65536, "bf16", None),
+])
+def test_split_plans(M, N, K, fmt, splits):
+    p = dg.gemm_ex_plan(fmt, M, N, K, 1 << 40)
+    if splits is not None:
+        assert p["splits"] == splits and p["workspace_bytes"] == 0
+        return
+    assert p["splits"] > 1
+    ldw = -(-N // 4) * 4
+    assert p["workspace_bytes"] == p["splits"] * M * ldw * 4
+    # less workspace than the best plan wants: a plan that fits, possibly unsplit
+    q = dg.gemm_ex_plan(fmt, M, N, K, p["workspace_bytes"] - 1)
+    assert q["workspace_bytes"] <= p["workspace_bytes"] - 1
+    assert q["splits"] < p["splits"] or (q["tile_rows"], q["tile_cols"]) != \
+        (p["tile_rows"], p["tile_cols"])

@@ -1,0 +1,188 @@
+"""gemm_ex on the GPU: the fused epilogue (alpha, beta, bias, ReLU) and split-K
+plans, through the C ABI, against the oracle.
+
+Epilogue results are compared with oracle.epilogue (fp64) within
+oracle.parity.bound_epilogue; split-K results with the plain GEMM bound (the
+split only changes the fp32 summation order), bit for bit where the inputs are
+integers.  C is prefilled with NaN (so beta = 0 must never read it) and its row
+pitch gap must stay NaN; the workspace bytes past what the plan uses must stay
+untouched."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_matrix_amd as dg
+import oracle
+from oracle.parity import TOL_MFMA, bound_epilogue
+from synth_inputs import draw, pair
+from tests.gpu_util import TORCH, dev_matrix, gap_untouched, round_pitch, sentinel_c, to64
+from synth_inputs import to_torch as to_torch_cpu
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [("f32", "f32"), ("f32x3", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
+         ("f16", "f16")]
+PLAIN = {"f32": dg.gemm_f32, "f32x3": dg.gemm_f32_3xbf16, "bf16": dg.gemm_bf16,
+         "f16": dg.gemm_f16}
+
+
+def store(path):
+    return "f32" if path == "f32x3" else path
+
+
+def run_ex(path, out, A, B, *, alpha=1.0, beta=0.0, Cold=None, bias=None, relu=False,
+           ws_bytes=0, spare=4096):
+    """gemm_ex on seeded storage arrays; returns (C, workspace tensor or None)."""
+    M, K = A.shape
+    N = B.shape[1]
+    dtype = store(path)
+    Ad = dev_matrix(A, dtype, round_pitch(K, dtype, 8))
+    Bd = dev_matrix(B, dtype, round_pitch(N, dtype, 8))
+    Cd = sentinel_c(M, N, out)
+    if Cold is not None:
+        Cd[:] = to_torch_cpu(Cold, out).to("cuda")
+    bd = torch.from_numpy(np.asarray(bias, dtype=np.float32)).to("cuda") if bias is not None \
+        else None
+    ws = None
+    if ws_bytes:
+        ws = torch.full(((ws_bytes + spare) // 4,), float("nan"), dtype=torch.float32,
+                        device="cuda")
+    torch.cuda.synchronize()
+    dg.gemm_ex(Ad, Bd, Cd, alpha=alpha, beta=beta, bias=bd, relu=relu,
+               workspace=None if ws is None else ws[: ws_bytes // 4],
+               in_fmt="f32x3" if path == "f32x3" else None)
+    torch.cuda.synchronize()
+    return Cd, ws
+
+
+def spare_untouched(ws, used_bytes):
+    return ws is None or bool(torch.isnan(ws[used_bytes // 4:]).all().item())
+
+
+@pytest.mark.parametrize("path,out", PATHS)
+def test_identity_epilogue_equals_the_plain_entry_point(path, out):
+    A, B = pair(300, 264, 200, "normal", store(path), seed=5000)
+    C, _ = run_ex(path, out, A, B)
+    dtype = store(path)
+    Ad, Bd = dev_matrix(A, dtype), dev_matrix(B, dtype)
+    Cp = sentinel_c(300, 264, out)
+    PLAIN[path](Ad, Bd, Cp)
+    torch.cuda.synchronize()
+    assert torch.equal(C, Cp)
+
+
+EPIS = [(-1.5, 0.0, True, False), (1.0, 0.5, False, True), (0.75, -1.0, True, True)]
+
+
+@pytest.mark.parametrize("path,out", PATHS)
+@pytest.mark.parametrize("M,N,K", [(257, 300, 65), (33, 7, 257), (256, 256, 64)])
+def test_epilogue_parity(path, out, M, N, K):
+    rng = np.random.default_rng(5100 + M + N + K + PATHS.index((path, out)))
+    dtype = store(path)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    C64, S = oracle.gemm(dtype, A, B)
+    for alpha, beta, use_bias, relu in EPIS:
+        print(f"case epilogue {path}->{out} {M}x{N}x{K} a={alpha} b={beta} bias={use_bias} "
+              f"relu={relu}", flush=True)
+        Cold = draw(rng, (M, N), "normal", out) if beta != 0.0 else None
+        bias = rng.standard_normal(N).astype(np.float32) if use_bias else None
+        C, _ = run_ex(path, out, A, B, alpha=alpha, beta=beta, Cold=Cold, bias=bias, relu=relu)
+        E, T = oracle.epilogue(C64, alpha, beta, None if Cold is None else oracle.widen(out, Cold),
+                               None if bias is None else bias.astype(np.float64), relu)
+        b = bound_epilogue(E, T, S, alpha, TOL_MFMA, out)
+        res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
+        assert res["ok"], res
+        assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("path,out", PATHS)
+def test_k_zero_applies_the_epilogue_to_the_empty_sum(path, out):
+    rng = np.random.default_rng(5200)
+    M, N = 70, 90
+    dtype = store(path)
+    A = np.zeros((M, 0), dtype=draw(rng, (1, 1), "normal", dtype).dtype)
+    B = np.zeros((0, N), dtype=A.dtype)
+    Cold = draw(rng, (M, N), "normal", out)
+    bias = rng.standard_normal(N).astype(np.float32)
+    C, _ = run_ex(path, out, A, B, alpha=3.0, beta=-0.5, Cold=Cold, bias=bias, relu=True)
+    E, T = oracle.epilogue(np.zeros((M, N)), 3.0, -0.5, oracle.widen(out, Cold),
+                           bias.astype(np.float64), True)
+    b = bound_epilogue(E, T, np.zeros((M, N)), 3.0, TOL_MFMA, out)
+    assert oracle.check(to64(C), E, np.zeros((M, N)), TOL_MFMA, out, b=b)["ok"]
+
+
+# Shapes whose best plan splits K, with the workspace it asks for.
+SPLIT_CASES = [("f32", "f32", 512, 512, 512), ("f32x3", "f32", 512, 512, 512),
+               ("bf16", "f32", 64, 64, 4096), ("bf16", "bf16", 200, 136, 3000),
+               ("f16", "f16", 64, 72, 4104), ("f16", "f32", 256, 256, 16384)]
+
+
+def split_plan(path, out, M, N, K):
+    p = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(out != "f32"))
+    assert p["splits"] > 1, p
+    return p
+
+
+@pytest.mark.parametrize("path,out,M,N,K", SPLIT_CASES)
+def test_split_k_parity(path, out, M, N, K):
+    p = split_plan(path, out, M, N, K)
+    print(f"case splitk {path}->{out} {M}x{N}x{K} plan {p}", flush=True)
+    dtype = store(path)
+    A, B = pair(M, N, K, "normal", dtype, seed=5300 + M + K)
+    C, ws = run_ex(path, out, A, B, ws_bytes=p["workspace_bytes"])
+    C64, S = oracle.gemm(dtype, A, B)
+    res = oracle.check(to64(C), C64, S, TOL_MFMA, out)
+    assert res["ok"], res
+    assert gap_untouched(C) and spare_untouched(ws, p["workspace_bytes"])
+
+
+@pytest.mark.parametrize("path,out,M,N,K", SPLIT_CASES)
+def test_split_k_with_epilogue(path, out, M, N, K):
+    p = split_plan(path, out, M, N, K)
+    rng = np.random.default_rng(5400 + M + K)
+    dtype = store(path)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    Cold = draw(rng, (M, N), "normal", out)
+    bias = rng.standard_normal(N).astype(np.float32)
+    C, ws = run_ex(path, out, A, B, alpha=0.5, beta=2.0, Cold=Cold, bias=bias, relu=True,
+                   ws_bytes=p["workspace_bytes"])
+    C64, S = oracle.gemm(dtype, A, B)
+    E, T = oracle.epilogue(C64, 0.5, 2.0, oracle.widen(out, Cold), bias.astype(np.float64), True)
+    b = bound_epilogue(E, T, S, 0.5, TOL_MFMA, out)
+    res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
+    assert res["ok"], res
+    assert gap_untouched(C) and spare_untouched(ws, p["workspace_bytes"])
+
+
+@pytest.mark.parametrize("path,out,M,N,K", SPLIT_CASES)
+def test_split_k_exact_integers_bitwise_and_repeatable(path, out, M, N, K):
+    """Integer inputs keep every partial sum exact in fp32, so the split result
+    must equal the oracle's rounding bit for bit; a second run must repeat it."""
+    p = split_plan(path, out, M, N, K)
+    dtype = store(path)
+    A, B = pair(M, N, K, "ints", dtype, seed=5500 + M + K)
+    C1, _ = run_ex(path, out, A, B, ws_bytes=p["workspace_bytes"])
+    C2, _ = run_ex(path, out, A, B, ws_bytes=p["workspace_bytes"])
+    C64, _ = oracle.gemm(dtype, A, B)
+    assert np.max(np.abs(C64)) < 2 ** 24   # |a b| <= 64 and K <= 16384
+    assert np.array_equal(to64(C1), oracle.widen(out, oracle.round_to(out, C64)))
+    assert torch.equal(C1, C2)
+
+
+def test_one_gpu_row_share_of_4096_cubed():
+    """512 x 4096 x 4096 bf16 (one GPU's share of 4096^3 split by rows over 8):
+    the split plan through matmul, sampled rows against the oracle, and every
+    element written."""
+    M, N, K = 512, 4096, 4096
+    p = split_plan("bf16", "bf16", M, N, K)
+    A, B = pair(M, N, K, "normal002", "bf16", seed=5600)
+    Ad, Bd = dev_matrix(A, "bf16", K), dev_matrix(B, "bf16", N)
+    C = dg.matmul(Ad, Bd)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(C.float()).any().item())
+    rows = np.array([0, 1, 31, 127, 128, 255, 256, 300, 383, 384, 510, 511])
+    C64, S = oracle.gemm("bf16", A, B, rows=rows)
+    res = oracle.check(to64(C[torch.from_numpy(rows).to("cuda")]), C64, S, TOL_MFMA, "bf16")
+    assert res["ok"], (p, res)
