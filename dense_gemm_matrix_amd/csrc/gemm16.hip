@@ -259,6 +259,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // flight) and barrier, which retires every wave's reads of stage kt % S16;
     // then, spread over the MFMAs of pairs 1 .. KP16 - 1, refill that stage
     // with step kt + S16, and during the last pair read pair 0 of step kt + 1.
+    // The last step reads that pair too (from the stage the empty loads past
+    // K have zero-filled, inside the LDS array; the registers are never
+    // used): an unconditional read saves a branch per matrix instruction.
     if (nk > 0) {
 #pragma unroll
         for (int s = 0; s < S16; ++s) issue_stage(s);
@@ -282,7 +285,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
             const StageDesc d = stage_desc(kt + S16);
             sync(TwoStepsLeft{});
             if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            const bool more = kt + 1 < nk;
             constexpr int SLOTS = T::NMFMA * (KP16 - 1);
 #pragma unroll
             for (int kp = 1; kp < KP16; ++kp) {
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
                     for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
                         dma_one(d, j);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (kp == KP16 - 1 && more) {
+                    if (kp == KP16 - 1) {
 #pragma unroll
                         for (int r = (i * T::NREAD) / T::NMFMA; r < ((i + 1) * T::NREAD) / T::NMFMA; ++r)
                             read_piece(kt + 1, 0, fa[0], fb[0], r);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     store_tile<OUT, MI, NJ, EPI>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / 2), g, li,
-                                 epi);
+                                 epi, m0 + TBM <= M && n0 + TBN <= N);
 }
 
 template <int IN, int OUT, int TBM, int TBN, bool EPI>

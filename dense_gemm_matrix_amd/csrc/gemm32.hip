@@ -202,7 +202,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
         }
     }
 
-    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi);
+    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi,
+                                   m0 + BM <= M && n0 + BN <= N);
 }
 
 // ---------------------------------------------------------------- fp32 via 3 x bf16
@@ -406,7 +407,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         }
     }
 
-    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi);
+    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi,
+                                   m0 + BM <= M && n0 + BN <= N);
 }
 
 hipError_t go(const void* fn, const GemmLaunch& L) {

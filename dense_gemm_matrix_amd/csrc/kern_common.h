@@ -105,22 +105,25 @@ __device__ __forceinline__ float epilogue(float s, const char* C, int64_t idx, f
 }
 
 // Epilogue of the GEMM kernels.  32x32 accumulator layout: lane (g, li) holds
-// column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4.
-template <int OUT, int MI, int NJ, bool EPI>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
-                                           int ldc, int row0, int col0, int g, int li,
-                                           const EpiArgs& e) {
+// column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4.  Elements
+// outside M x N are not stored; `full` (the whole macro-tile lies inside, a
+// wave-uniform fact) takes a copy of the loop without the per-element tests,
+// which would otherwise become one branch per store.
+template <int OUT, int MI, int NJ, bool EPI, bool FULL>
+__device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
+                                                int ldc, int row0, int col0, int g, int li,
+                                                const EpiArgs& e) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
             const int col = col0 + nj * 32 + li;
             float bias = 0.0f;
-            if (EPI && e.bias && col < N) bias = e.bias[col];
+            if (EPI && e.bias && (FULL || col < N)) bias = e.bias[col];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (row < M && col < N) {
+                if (FULL || (row < M && col < N)) {
                     const int64_t idx = (int64_t)row * ldc + col;
                     float v = acc[mi][nj][r];
                     if constexpr (EPI) v = epilogue<OUT>(v, C, idx, bias, e);
@@ -129,6 +132,16 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C,
             }
         }
     }
+}
+
+template <int OUT, int MI, int NJ, bool EPI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
+                                           int ldc, int row0, int col0, int g, int li,
+                                           const EpiArgs& e, bool full) {
+    if (full)
+        store_tile_impl<OUT, MI, NJ, EPI, true>(acc, C, M, N, ldc, row0, col0, g, li, e);
+    else
+        store_tile_impl<OUT, MI, NJ, EPI, false>(acc, C, M, N, ldc, row0, col0, g, li, e);
 }
 
 }  // namespace dgemm
