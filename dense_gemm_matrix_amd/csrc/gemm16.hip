@@ -42,24 +42,28 @@ constexpr int A16_CH = BK16 / 8;               // 16-byte chunks per A row
 constexpr int A16_ROW = BK16 * 2;              // bytes per staged A row
 constexpr int A16_RPB = 1024 / A16_ROW;        // A rows per 1 KiB load block
 
-// Macro-tile TBM x TBN, 4 waves in a 2 x 2 layout, each wave (TBM/2) x (TBN/2)
-// = MI x NJ blocks of 32 x 32 accumulators.
-template <int TBM, int TBN>
+// Macro-tile TBM x TBN, 2 x WN waves (WN = 2: 4 waves, one per SIMD; WN = 4:
+// 8 waves, two per SIMD), each wave (TBM/2) x (TBN/WN) = MI x NJ blocks of
+// 32 x 32 accumulators.
+template <int TBM, int TBN, int WN = 2>
 struct Tile16 {
+    static constexpr int NW = 2 * WN;                    // waves
+    static constexpr int NT = 64 * NW;                   // threads
     static constexpr int MI = TBM / 64;
-    static constexpr int NJ = TBN / 64;
+    static constexpr int NJ = TBN / (32 * WN);
     static constexpr int A_STAGE = TBM * A16_ROW;        // bytes per A stage
     static constexpr int B_ROW = TBN * 2;                // bytes per staged B row
     static constexpr int B_CH = TBN / 8;                 // 16-byte chunks per B row
     static constexpr int B_STAGE = BK16 * B_ROW;         // bytes per B stage
     static constexpr int B_RPB = 1024 / B_ROW;           // B rows per 1 KiB load block
-    static constexpr int A_DMA = A_STAGE / 1024 / 4;     // direct-to-LDS loads per wave per stage
-    static constexpr int B_DMA = B_STAGE / 1024 / 4;
+    static constexpr int A_DMA = A_STAGE / 1024 / NW;    // direct-to-LDS loads per wave per stage
+    static constexpr int B_DMA = B_STAGE / 1024 / NW;
     static constexpr int LOADS = A_DMA + B_DMA;
     static constexpr int NREAD = MI + 2 * NJ;            // fragment reads per chunk pair
     static constexpr int NMFMA = MI * NJ;                // MFMAs per chunk pair
-    static_assert(TBM % 64 == 0 && TBN % 64 == 0 && TBM <= NTHREADS, "tile shape");
-    static_assert(A_STAGE % 4096 == 0 && B_STAGE % 4096 == 0, "whole load blocks per wave");
+    static_assert(TBM % 64 == 0 && TBN % (32 * WN) == 0 && TBM <= NT, "tile shape");
+    static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0,
+                  "whole load blocks per wave");
     static_assert(S16 * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
     static_assert((S16 - 1) * LOADS <= 63, "vmcnt range");
 };
@@ -81,12 +85,12 @@ __device__ __forceinline__ int b16_off(int k, int chunk, int row_bytes) {
     return k * row_bytes + ((chunk ^ b16_swz(k)) << 4);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI>
-__global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
+template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN>
+__global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
     int kchunk, int64_t c_zstride, EpiArgs epi) {
-    using T = Tile16<TBM, TBN>;
+    using T = Tile16<TBM, TBN, WN>;
     // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
     // and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when unsplit).
     {
@@ -186,8 +190,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
         }
     };
 
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
     const int g = lane >> 5;          // lane group: k half of a 16-k chunk pair
     const int li = lane & 31;         // row of A within a 32-row block
     const int ta = (lane >> 2) & 3;   // transpose read: source k row within the group
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
             const char* sb = smB + (kt % S16) * T::B_STAGE;
             const int nj = (i - MI) >> 1, h = (i - MI) & 1;
             const int k = kp * 16 + 8 * g + 4 * h + ta;
-            const int c = wn * (TBN / 16) + nj * 4 + 2 * tg + (tq >> 1);
+            const int c = wn * (TBN / WN / 8) + nj * 4 + 2 * tg + (tq >> 1);
             b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s16x4_t*)(sb + b16_off(k, c, T::B_ROW) + (tq & 1) * 8));
         }
@@ -310,11 +314,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm16_kernel(
     // No direct-to-LDS write may still be in flight when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-    store_tile<OUT, MI, NJ, EPI>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / 2), g, li,
+    store_tile<OUT, MI, NJ, EPI>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / WN), g, li,
                                  epi, m0 + TBM <= M && n0 + TBN <= N);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI>
+template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN = 2>
 hipError_t go(const GemmLaunch& L) {
     const char* a = L.A;
     const char* b = L.B;
@@ -324,8 +328,9 @@ hipError_t go(const GemmLaunch& L) {
     int64_t zs = L.c_zstride;
     EpiArgs e = L.e;
     void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &kchunk, &zs, &e};
-    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI>,
-                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits), dim3(NTHREADS),
+    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI, WN>,
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits),
+                           dim3(Tile16<TBM, TBN, WN>::NT),
                            args, 0, L.stream);
 }
 

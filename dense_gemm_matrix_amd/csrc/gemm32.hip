@@ -278,14 +278,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 
     u32x4 ra[8], rb[8];
 
-    auto load_step = [&](int kt, bool tail) {
+    // Global loads of step kt into registers.  Steps at or past the end get
+    // empty ranges and load zeros (the schedule below issues them
+    // unconditionally; their data is never used).
+    auto load_step = [&](int kt) {
         const int k0 = kt * BK;
+        const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
-        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
+        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 4 : 0;
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
-        const int rows_b = (K - k0) < BK ? (K - k0) : BK;
+        const int rows_b = krem < BK ? krem : BK;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
-        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
+        const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -294,46 +298,38 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
-        if (tail) {
-            // Columns of A at or past K hold other data (row padding or the next
-            // row); they must be exact zeros, since the matching B rows are.
-            const int valid = K - k0 - ac * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[2 * i] = mask_tail32(ra[2 * i], valid);
-                ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
-            }
-        }
     };
 
-    auto store_step = [&](int s) {
+    // Store unit u (0..7) of step kt into stage s: u < 4 splits A row
+    // ar0 + 64 u (masking columns at or past K when `tail`: they hold other
+    // data, row padding or the next row, and must be exact zeros since the
+    // matching B rows are); u >= 4 splits column u - 4 of the B block (8
+    // consecutive k -> one chunk per part).
+    auto store_unit = [&](int s, int u, int kt, bool tail) {
         char* st = smem + s * X3_STAGE;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x[8];
+        float x[8];
+        if (u < 4) {
+            u32x4 p0 = ra[2 * u], p1 = ra[2 * u + 1];
+            if (tail) {
+                const int valid = K - kt * BK - ac * 8;
+                p0 = mask_tail32(p0, valid);
+                p1 = mask_tail32(p1, valid - 4);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = as_float(ra[2 * i][e]);
-                x[4 + e] = as_float(ra[2 * i + 1][e]);
+                x[e] = as_float(p0[e]);
+                x[4 + e] = as_float(p1[e]);
             }
-            u32x4 hi, lo;
-            split8(x, hi, lo);
-            const int off = x3_off(ar0 + 64 * i, ac);
-            *(u32x4*)(st + off) = hi;
-            *(u32x4*)(st + X3_PART + off) = lo;
-        }
-        // B: column cc of the block, 8 consecutive k -> one chunk per part.
+        } else {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = as_float(rb[e][cc]);
-            u32x4 hi, lo;
-            split8(x, hi, lo);
-            const int off = x3_off(nb * 4 + cc, kb);
-            *(u32x4*)(st + 2 * X3_PART + off) = hi;
-            *(u32x4*)(st + 3 * X3_PART + off) = lo;
+            for (int e = 0; e < 8; ++e) x[e] = as_float(rb[e][u - 4]);
         }
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        const int off = u < 4 ? x3_off(ar0 + 64 * u, ac) : x3_off(nb * 4 + (u - 4), kb);
+        char* base = st + (u < 4 ? 0 : 2 * X3_PART);
+        *(u32x4*)(base + off) = hi;
+        *(u32x4*)(base + X3_PART + off) = lo;
     };
 
     const int wm = wave >> 1;
@@ -352,58 +348,75 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     // Fragments of one 16-k chunk pair: [part][block], part 0 = hi, 1 = lo.
     u32x4 fa[2][2][4], fb[2][2][4];
 
-    auto read_frags = [&](int s, int kp, u32x4 (&a)[2][4], u32x4 (&b)[2][4]) {
+    // Fragment read r (0..15) of pair kp from stage s: part r / 8; A block
+    // r % 8 when r % 8 < 4, else B block r % 8 - 4.
+    auto read_one = [&](int s, int kp, u32x4 (&a)[2][4], u32x4 (&b)[2][4], int r) {
         const char* st = smem + s * X3_STAGE;
         const int ch = 2 * kp + g;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                a[p][mi] = *(const u32x4*)(st + p * X3_PART + x3_off(wm * 128 + mi * 32 + li, ch));
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
-                b[p][nj] = *(const u32x4*)(st + (2 + p) * X3_PART + x3_off(wn * 128 + nj * 32 + li, ch));
-        }
+        const int p = r >> 3, q = r & 7;
+        if (q < 4)
+            a[p][q] = *(const u32x4*)(st + p * X3_PART + x3_off(wm * 128 + q * 32 + li, ch));
+        else
+            b[p][q - 4] = *(const u32x4*)(st + (2 + p) * X3_PART + x3_off(wn * 128 + (q - 4) * 32 + li, ch));
     };
 
-    auto mfma_frags = [&](const u32x4 (&a)[2][4], const u32x4 (&b)[2][4]) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj) {
-                // small terms first, then the leading one
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, a[1][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[1][nj]), acc[mi][nj], 0, 0, 0);
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, a[0][mi]), __builtin_bit_cast(bf16x8, b[0][nj]), acc[mi][nj], 0, 0, 0);
-            }
-        }
+    // Matrix instruction i (0..47) of a pair: block i / 3 (mi, nj), product
+    // i % 3: the small terms first, then the leading one.
+    auto mfma_one = [&](const u32x4 (&a)[2][4], const u32x4 (&b)[2][4], int i) {
+        const int mi = (i / 3) >> 2, nj = (i / 3) & 3, t = i % 3;
+        const u32x4 av = t == 1 ? a[0][mi] : (t == 0 ? a[1][mi] : a[0][mi]);
+        const u32x4 bv = t == 1 ? b[1][nj] : b[0][nj];
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[mi][nj], 0, 0, 0);
     };
 
-    // Per step: global loads of step kt + 1 -> registers; read pair 1 while
-    // pair 0 computes; split and write step kt + 1 to the other stage;
-    // barrier; read pair 0 of step kt + 1 while pair 1 computes.
+    // Schedule of step kt (stage cur holds it, stage cur ^ 1 receives step
+    // kt + 1), in issue order; sched_barrier pins it:
+    //   global loads of step kt + 1 into registers;
+    //   pair 0's 48 MFMAs, the first 16 each followed by one read of pair 1,
+    //   the last 24 by a store unit every 6 (A rows: split, write hi and lo);
+    //   pair 1's first 24 MFMAs, a store unit every 6 (B columns);
+    //   barrier (stage cur ^ 1 complete; every read of stage cur issued);
+    //   pair 1's last 24 MFMAs, the first 16 each followed by one read of
+    //   step kt + 1's pair 0.
+    // The split and convert work (about 30 VALU instructions per unit) thus
+    // runs in the shadow of the matrix instructions.  The last step also loads,
+    // stores and reads "step nk" (zeros, inside the LDS array; never used).
     if (nk > 0) {
-        load_step(0, ragged_k && nk == 1);
-        store_step(0);
+        load_step(0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) store_unit(0, u, 0, ragged_k && nk == 1);
         __syncthreads();
-        read_frags(0, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) read_one(0, 0, fa[0], fb[0], r);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
-            read_frags(cur, 1, fa[1], fb[1]);
+            const bool tail_next = ragged_k && kt + 2 == nk;
+            load_step(kt + 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[0], fb[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (more) store_step(cur ^ 1);
+#pragma unroll
+            for (int i = 0; i < 48; ++i) {
+                mfma_one(fa[0], fb[0], i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i < 16) read_one(cur, 1, fa[1], fb[1], i);
+                if (i >= 24 && (i - 24) % 6 == 0) store_unit(cur ^ 1, (i - 24) / 6, kt + 1, tail_next);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < 24; ++i) {
+                mfma_one(fa[1], fb[1], i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i % 6 == 0) store_unit(cur ^ 1, 4 + i / 6, kt + 1, false);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             __syncthreads();
-            if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[1], fb[1]);
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 24; i < 48; ++i) {
+                mfma_one(fa[1], fb[1], i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i - 24 < 16) read_one(cur ^ 1, 0, fa[0], fb[0], i - 24);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
