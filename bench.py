@@ -6,7 +6,9 @@ the swizzled layout, the matrix-instruction loop and the epilogue all run inside
 that one kernel) on inputs already resident in HBM.  The headline line is the
 bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
 fp32-input 4096^3 products are measured the same way and reported under
-"per_dtype".  The other parity workloads, and one GPU's row share of the 4096^3
+"per_dtype".  Also reported: the same product from a cold cache (each launch
+after a 512 MiB write), and the graphics clock and socket power amd-smi reads
+while the product runs.  The other parity workloads, and one GPU's row share of the 4096^3
 product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
 the planner splits K, through gemm_ex with a workspace.
 
@@ -129,6 +131,76 @@ def cpu_baseline(A, B, meta, target_s: float = 12.0):
                       f"{t:.1f} s"}
 
 
+def _smi_values(node, key):
+    """All numeric 'value' fields under dict keys starting with `key`."""
+    out = []
+    if isinstance(node, dict):
+        for k, v in node.items():
+            if k.startswith(key) and isinstance(v, dict):
+                inner = v.get("clk", v)
+                val = inner.get("value") if isinstance(inner, dict) else None
+                if isinstance(val, (int, float)):
+                    out.append(float(val))
+            else:
+                out += _smi_values(v, key)
+    elif isinstance(node, list):
+        for v in node:
+            out += _smi_values(v, key)
+    return out
+
+
+def cold_cache(entry, Ad, Bd, Cd, launches: int = 20):
+    """Mean time of single launches, each after writing a 512 MiB buffer (which
+    evicts A, B and C from L2 and the 256 MB MALL)."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    total = 0.0
+    for _ in range(launches):
+        scratch.fill_(1)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        entry(Ad, Bd, Cd, stream=stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        total += start.elapsed_time(stop) * 1e-3
+    del scratch
+    return total / launches
+
+
+def power_clock(entry, Ad, Bd, Cd, per_launch_s: float, value_tflops: float, peak: float):
+    """Graphics clock and socket power while the GEMM runs: about 1.5 s of
+    launches are queued, amd-smi (a child process) samples the device, then the
+    queue drains.  None when amd-smi is missing or fails."""
+    import subprocess
+    import torch
+    n = int(min(50000, max(1000, 1.5 / max(per_launch_s, 1e-6))))
+    stream = torch.cuda.current_stream()
+    for _ in range(n):
+        entry(Ad, Bd, Cd, stream=stream)
+    try:
+        raw = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"],
+                             capture_output=True, text=True, timeout=60).stdout
+        data = json.loads(raw)
+    except Exception:  # noqa: BLE001 - any failure means "not measured"
+        data = None
+    torch.cuda.synchronize()
+    if data is None:
+        return None
+    clks = _smi_values(data, "gfx_")
+    power = _smi_values(data, "socket_power")
+    if not clks:
+        return None
+    sclk = sum(clks) / len(clks)
+    adj_peak = peak * sclk / 2400.0
+    return {"sclk_mhz_mean": round(sclk, 1), "sclk_mhz_per_xcd": clks,
+            "socket_power_w": power[0] if power else None,
+            "clock_adjusted_peak_tflops": round(adj_peak, 1),
+            "frac_of_clock_adjusted_peak": round(value_tflops / adj_peak, 4),
+            "how": f"amd-smi sampled once while {n} queued launches ran"}
+
+
 def copy_calibration(gib: float = 1.0, reps: int = 5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -199,6 +271,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-dtype", action="store_true")
     ap.add_argument("--no-shapes", action="store_true")
+    ap.add_argument("--no-power-clock", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -245,6 +318,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(value / peak, 4), "traffic": traffic},
     }
+    t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
+    line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
+                          "launches": 20, "how": "each launch after writing a 512 MiB buffer"}
+    if not args.no_power_clock:
+        print("bench: sampling clock and power under load", file=sys.stderr, flush=True)
+        line["power_clock"] = power_clock(entry[args.dtype], Ad, Bd, Cd, per_launch, value, peak)
     if not args.no_per_dtype:
         # The other dtypes of the metric, and fp32 inputs through the 3 x bf16
         # entry (its peak is the bf16 matrix peak: three bf16 products per term).
