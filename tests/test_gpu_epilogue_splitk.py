@@ -186,3 +186,62 @@ def test_one_gpu_row_share_of_4096_cubed():
     C64, S = oracle.gemm("bf16", A, B, rows=rows)
     res = oracle.check(to64(C[torch.from_numpy(rows).to("cuda")]), C64, S, TOL_MFMA, "bf16")
     assert res["ok"], (p, res)
+
+
+def test_split_k_on_a_non_default_stream_matches_the_default_stream():
+    """The split plan's two kernels are ordered on the caller's stream."""
+    M, N, K = 64, 64, 4096
+    p = split_plan("bf16", "bf16", M, N, K)
+    A, B = pair(M, N, K, "normal", "bf16", seed=5700)
+    Ad, Bd = dev_matrix(A, "bf16", K), dev_matrix(B, "bf16", N)
+    ws = torch.empty(p["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.gemm_ex(Ad, Bd, ref, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    got = torch.empty_like(ref)
+    ws2 = torch.empty_like(ws)
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            dg.gemm_ex(Ad, Bd, got, workspace=ws2, stream=s)
+    s.synchronize()
+    assert torch.equal(ref, got)
+
+
+def test_workspace_smaller_than_the_best_plan_still_gives_the_product():
+    """With less workspace than the preferred plan needs, gemm_ex picks a plan
+    that fits (here: unsplit) and the result still matches the oracle."""
+    M, N, K = 64, 64, 4096
+    best = split_plan("f16", "f16", M, N, K)
+    small = best["workspace_bytes"] // 4
+    fit = dg.gemm_ex_plan("f16", M, N, K, small, out_same=True)
+    assert fit["workspace_bytes"] <= small
+    A, B = pair(M, N, K, "normal", "f16", seed=5800)
+    C, ws = run_ex("f16", "f16", A, B, ws_bytes=small)
+    C64, S = oracle.gemm("f16", A, B)
+    assert oracle.check(to64(C), C64, S, TOL_MFMA, "f16")["ok"]
+    assert gap_untouched(C) and spare_untouched(ws, fit["workspace_bytes"])
+
+
+def test_full_size_ragged_workload_with_fused_epilogue():
+    """4000 x 3000 x 4104 (192 x 256 tiles, ragged in every dimension) with
+    alpha, beta, bias and ReLU, bf16 C: sampled rows against the oracle."""
+    from synth_inputs import workload
+    A, B, meta = workload("bf16_4000x3000x4104")
+    M, N, K = meta["M"], meta["N"], meta["K"]
+    rng = np.random.default_rng(5900)
+    Cold = draw(rng, (M, N), "normal", "bf16")
+    bias = rng.standard_normal(N).astype(np.float32) * 0.1
+    Ad, Bd = dev_matrix(A, "bf16", K), dev_matrix(B, "bf16", N)
+    C = to_torch_cpu(Cold, "bf16").to("cuda")
+    dg.gemm_ex(Ad, Bd, C, alpha=2.0, beta=-0.5, bias=torch.from_numpy(bias).to("cuda"),
+               relu=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 191, 192, 2047, 3839, 3840, 3999])
+    C64, S = oracle.gemm("bf16", A, B, rows=rows)
+    E, T = oracle.epilogue(C64, 2.0, -0.5, oracle.widen("bf16", Cold[rows]),
+                           bias.astype(np.float64), True)
+    b = bound_epilogue(E, T, S, 2.0, TOL_MFMA, "bf16")
+    got = to64(C[torch.from_numpy(rows).to("cuda")])
+    res = oracle.check(got, E, S, TOL_MFMA, "bf16", b=b)
+    assert res["ok"], res
