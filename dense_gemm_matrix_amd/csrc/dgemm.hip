@@ -94,7 +94,16 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 
 struct TileCand { int bm, bn; double eff; };
 constexpr TileCand TILES16[] = {{256, 256, 1.0}, {192, 256, 0.95}, {128, 128, 0.6}};
-constexpr TileCand TILES32[] = {{256, 256, 1.0}};
+constexpr TileCand TILES32[] = {{256, 256, 1.0}, {128, 128, 0.85}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0}};
+
+// Candidate macro-tiles of an input format's kernel.
+const TileCand* tiles_for(int in, int& n) {
+    if (in == IN_BF16 || in == IN_F16) { n = 3; return TILES16; }
+    if (in == IN_F32) { n = 2; return TILES32; }
+    n = 1;
+    return TILES32X3;
+}
 
 // Microseconds per K step of one 256 x 256 workgroup at 4096^3.
 double step_us(int in) {
@@ -119,10 +128,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // on M, N and the input format only, so the host query reports exactly what
 // an unsplit launch uses.
 TileCand pick_tile(int in, int M, int N) {
-    if (in == IN_F32 || in == IN_F32X3) return TILES32[0];
-    TileCand best = TILES16[0];
+    int n = 0;
+    const TileCand* cands = tiles_for(in, n);
+    TileCand best = cands[0];
     double best_cost = -1.0;
-    for (const TileCand& c : TILES16) {
+    for (int i = 0; i < n; ++i) {
+        const TileCand& c = cands[i];
         const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
         const double cost = (double)ceil_div(tiles, NUM_CU) * c.bm * c.bn / c.eff;
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c; }
@@ -150,9 +161,8 @@ Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail) {
     const int nk = (int)ceil_div(K, bk);
     const int ldw = (int)ceil_div(N, 4) * 4;
     double best = estimate_us(in, es_out, M, N, base, 1, nk, ldw) * SPLIT_MARGIN;
-    const bool is16 = in == IN_BF16 || in == IN_F16;
-    const TileCand* cands = is16 ? TILES16 : TILES32;
-    const int ncand = is16 ? 3 : 1;
+    int ncand = 0;
+    const TileCand* cands = tiles_for(in, ncand);
     for (int c = 0; c < ncand; ++c) {
         for (int s = 2; s <= MAX_SPLITS && s <= nk; ++s) {
             const int steps = (int)ceil_div(nk, s);

@@ -36,7 +36,6 @@ __device__ __forceinline__ void split_k_window(const char* __restrict__& A,
 }
 
 constexpr int ROW_CHUNKS32 = 8;                  // 16-byte chunks per staged row (32 fp32)
-constexpr int STAGE_CHUNKS32 = BM * ROW_CHUNKS32;  // one operand's stage: 32 KiB
 
 // LDS slot of chunk c in staged row r.  With phi(r) = (r ^ (r >> 3)) & 7, the 8
 // consecutive rows an operand read touches get 8 distinct slots, and so do the
@@ -53,43 +52,50 @@ __device__ __forceinline__ u32x4 mask_tail32(u32x4 v, int valid) {
     return out;
 }
 
-template <bool EPI>
+// Square TB x TB macro-tile (256 or 128), 4 waves in a 2 x 2 layout, each wave
+// (TB/2)^2 = MI x MI blocks of 32 x 32 accumulators.  Staging per step: A is
+// TB rows x 8 chunks, thread -> chunk ac of rows ar0 + 32 i (i < TB / 32); B is
+// 32 k-rows x TB columns, thread -> a block of KB k-rows x 4 columns, KB = 8 at
+// TB = 256 and 4 at TB = 128 (256 blocks either way), transposed on its way
+// through registers so that both operands are stored K-contiguous.
+template <bool EPI, int TB>
 __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
     int kchunk, int64_t c_zstride, EpiArgs epi) {
+    static_assert(TB == 256 || TB == 128, "tile");
+    constexpr int MI = TB / 64;               // 32 x 32 blocks per wave per dimension
+    constexpr int NA = TB / 32;               // A chunks per thread per step
+    constexpr int KB = TB == 256 ? 8 : 4;     // B k-rows per thread block
+    constexpr int STAGE_CHUNKS = TB * ROW_CHUNKS32;
     split_k_window(A, B, C, K, ldb, kchunk, c_zstride);
-    // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x 32 KiB.  Both operands are
-    // stored K-contiguous: B is transposed on its way through registers.
-    __shared__ u32x4 lds[2][2][STAGE_CHUNKS32];
+    // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x (TB / 8) KiB.
+    __shared__ u32x4 lds[2][2][STAGE_CHUNKS];
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
-    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int m0 = tm * TB;
+    const int n0 = tn * TB;
+    const int rows_a = (M - m0) < TB ? (M - m0) : TB;
+    const int cols_b = (N - n0) < TB ? (N - n0) : TB;
     const int nk = (K + BK - 1) / BK;
     const bool ragged_k = (K % BK) != 0;
 
-    // A staging: thread -> chunk ac of rows ar0 + 32 i, i = 0..7.
     const int ac = tid & 7;
     const int ar0 = tid >> 3;
-    // B staging: thread -> a block of 8 K-rows (kb) by 4 columns (nb).
-    const int kb = tid & 3;
-    const int nb = tid >> 2;
+    const int kb = tid % (BK / KB);
+    const int nb = tid / (BK / KB);
 
-    int voff_a[8], voff_b[8];
+    int voff_a[NA], voff_b[KB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        voff_a[i] = (ar0 + 32 * i) * lda * 4 + ac * 16;
-        voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
-    }
+    for (int i = 0; i < NA; ++i) voff_a[i] = (ar0 + 32 * i) * lda * 4 + ac * 16;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) voff_b[i] = (kb * KB + i) * ldb * 4 + nb * 16;
 
-    u32x4 ra[8], rb[8];
+    u32x4 ra[NA], rb[KB];
 
     auto load_step = [&](int kt, bool tail) {
         const int k0 = kt * BK;
@@ -101,30 +107,30 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
         const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ra[i] = load16(rsa, voff_a[i]);
+        for (int i = 0; i < NA; ++i) ra[i] = load16(rsa, voff_a[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        for (int i = 0; i < KB; ++i) rb[i] = load16(rsb, voff_b[i]);
         if (tail) {
             // Columns of A at or past K hold other data (row padding or the next
             // row); they must be exact zeros, since the matching B rows are.
             const int valid = K - k0 - ac * 4;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ra[i] = mask_tail32(ra[i], valid);
+            for (int i = 0; i < NA; ++i) ra[i] = mask_tail32(ra[i], valid);
         }
     };
 
     auto store_step = [&](int s) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lds[s][0][lds32_index(ar0 + 32 * i, ac)] = ra[i];
-        // 8 K-rows x 4 columns -> 4 columns x two chunks of 4 K values.
+        for (int i = 0; i < NA; ++i) lds[s][0][lds32_index(ar0 + 32 * i, ac)] = ra[i];
+        // KB K-rows x 4 columns -> 4 columns x KB / 4 chunks of 4 K values.
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < KB / 4; ++h) {
                 u32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
-                lds[s][1][lds32_index(nb * 4 + cc, kb * 2 + h)] = v;
+                lds[s][1][lds32_index(nb * 4 + cc, kb * (KB / 4) + h)] = v;
             }
         }
     };
@@ -134,32 +140,34 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     const int g = lane >> 5;   // lane group: which chunk of a chunk pair
     const int li = lane & 31;  // row of A / column of B within a 32-block
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][MI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
+        for (int nj = 0; nj < MI; ++nj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
     // Operand fragments for one chunk pair (8 k): lane group g reads chunk
-    // 2 * kp + g of its 4 A rows and 4 B columns.  Two register sets alternate
-    // so that the reads for pair kp + 1 are in flight while kp computes.
-    u32x4 fa[2][4], fb[2][4];
+    // 2 * kp + g of its MI A rows and MI B columns.  Two register sets
+    // alternate so that the reads for pair kp + 1 are in flight while kp computes.
+    u32x4 fa[2][MI], fb[2][MI];
 
-    auto read_frags = [&](int s, int kp, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    auto read_frags = [&](int s, int kp, u32x4 (&a)[MI], u32x4 (&b)[MI]) {
         const int ch = 2 * kp + g;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) a[mi] = lds[s][0][lds32_index(wm * 128 + mi * 32 + li, ch)];
+        for (int mi = 0; mi < MI; ++mi)
+            a[mi] = lds[s][0][lds32_index(wm * (TB / 2) + mi * 32 + li, ch)];
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) b[nj] = lds[s][1][lds32_index(wn * 128 + nj * 32 + li, ch)];
+        for (int nj = 0; nj < MI; ++nj)
+            b[nj] = lds[s][1][lds32_index(wn * (TB / 2) + nj * 32 + li, ch)];
     };
 
-    auto mfma_frags = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+    auto mfma_frags = [&](const u32x4 (&a)[MI], const u32x4 (&b)[MI]) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
+            for (int nj = 0; nj < MI; ++nj)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
@@ -202,8 +210,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
         }
     }
 
-    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi,
-                                   m0 + BM <= M && n0 + BN <= N);
+    store_tile<OUT_F32, MI, MI, EPI>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
+                                     li, epi, m0 + TB <= M && n0 + TB <= N);
 }
 
 // ---------------------------------------------------------------- fp32 via 3 x bf16
@@ -440,9 +448,14 @@ hipError_t go(const void* fn, const GemmLaunch& L) {
 }  // namespace
 
 hipError_t launch_gemm32(const GemmLaunch& L) {
-    if (L.out != OUT_F32 || L.tbm != BM || L.tbn != BN) return hipErrorInvalidValue;
-    if (L.in == IN_F32)
-        return go(L.epi ? (const void*)gemm32_kernel<true> : (const void*)gemm32_kernel<false>, L);
+    if (L.out != OUT_F32 || L.tbm != L.tbn) return hipErrorInvalidValue;
+    if (L.in == IN_F32 && L.tbm == 256)
+        return go(L.epi ? (const void*)gemm32_kernel<true, 256> : (const void*)gemm32_kernel<false, 256>,
+                  L);
+    if (L.in == IN_F32 && L.tbm == 128)
+        return go(L.epi ? (const void*)gemm32_kernel<true, 128> : (const void*)gemm32_kernel<false, 128>,
+                  L);
+    if (L.tbm != BM) return hipErrorInvalidValue;
     if (L.in == IN_F32X3)
         return go(L.epi ? (const void*)gemm32x3_kernel<true> : (const void*)gemm32x3_kernel<false>,
                   L);
