@@ -12,7 +12,7 @@ namespace dgemm {
 enum InFmt { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2, IN_F32X3 = 3 };  // F32X3: fp32 via 3 x bf16
 enum OutFmt { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
-constexpr int NTHREADS = 256;   // 4 waves per workgroup in every GEMM kernel
+constexpr int NTHREADS = 256;   // 4 waves: the fp32 kernels' workgroup
 constexpr int GROUP_M = 4;      // tile rows per strip in the tile walk
 constexpr int NUM_XCD = 8;      // XCDs that workgroups are dealt across
 

@@ -11,10 +11,11 @@
 // column that the matrix instruction's B operand needs.
 // v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators.
 //
-// Per workgroup: 256 threads = 4 waves of 64 lanes in a 2 x 2 layout, each
-// wave owning a (TBM/2) x (TBN/2) sub-tile held as blocks of 32 x 32
-// accumulators (256 fp32 per lane at 256 x 256, register-resident for the
-// whole K loop).  LDS rows are split into 16-byte chunks whose positions are
+// Per workgroup as launched: 256 threads = 4 waves of 64 lanes in a 2 x 2
+// layout, one wave per SIMD, each wave owning a (TBM/2) x (TBN/2) sub-tile held
+// as blocks of 32 x 32 accumulators (256 fp32 per lane at 256 x 256,
+// register-resident for the whole K loop).  The template also builds a 2 x 4
+// layout of 8 waves (two per SIMD), which measured slower at 4096^3.  LDS rows are split into 16-byte chunks whose positions are
 // XORed with a function of the row, so every 16-byte access stays aligned (the
 // principle of the sgemm tf32 page's section 3 swizzles and the hgemm page's
 // section 2) while the access patterns used here hit distinct LDS banks.  The
