@@ -228,3 +228,33 @@ def test_split_plans(M, N, K, fmt, splits):
     assert q["workspace_bytes"] <= p["workspace_bytes"] - 1
     assert q["splits"] < p["splits"] or (q["tile_rows"], q["tile_cols"]) != \
         (p["tile_rows"], p["tile_cols"])
+
+
+# ---------------------------------------------------------------- planner properties
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=300, deadline=None)
+@given(M=st.integers(0, 20000), N=st.integers(0, 20000), K=st.integers(0, 70000),
+       fmt=st.sampled_from(["f32", "bf16", "f16", "f32x3"]),
+       ws=st.sampled_from([0, 1, 1 << 16, 1 << 20, 1 << 24, 1 << 28, 1 << 40]))
+def test_plan_invariants(M, N, K, fmt, ws):
+    p = dg.gemm_ex_plan(fmt, M, N, K, ws)
+    tiles = {"f32": {(256, 256), (128, 128)}, "bf16": {(256, 256), (192, 256), (128, 128)},
+             "f16": {(256, 256), (192, 256), (128, 128)}, "f32x3": {(256, 256)}}[fmt]
+    assert (p["tile_rows"], p["tile_cols"]) in tiles
+    assert 1 <= p["splits"] <= 16
+    assert p["workspace_bytes"] <= ws
+    if p["splits"] == 1:
+        assert p["workspace_bytes"] == 0
+        t = dg.dgemm_tile_map(M, N, fmt)
+        assert (p["tile_rows"], p["tile_cols"]) == (t["tile_rows"], t["tile_cols"])
+    else:
+        assert M > 0 and N > 0 and K > 0
+        assert p["workspace_bytes"] == p["splits"] * M * (-(-N // 4) * 4) * 4
+        bk = 64 if fmt in ("bf16", "f16") else 32
+        nk = -(-K // bk)
+        steps = -(-nk // p["splits"])
+        # every split gets at least one K step, and the splits cover K exactly once
+        assert (p["splits"] - 1) * steps < nk <= p["splits"] * steps

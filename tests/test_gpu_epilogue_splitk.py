@@ -245,3 +245,42 @@ def test_full_size_ragged_workload_with_fused_epilogue():
     got = to64(C[torch.from_numpy(rows).to("cuda")])
     res = oracle.check(got, E, S, TOL_MFMA, "bf16", b=b)
     assert res["ok"], res
+
+
+def random_cases(n=24, seed=6100):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        path, out = PATHS[int(rng.integers(len(PATHS)))]
+        M = int(rng.integers(1, 700))
+        N = int(rng.integers(1, 700))
+        K = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 6000))]))
+        alpha = float(rng.choice([1.0, -0.5, 1.25]))
+        beta = float(rng.choice([0.0, 0.0, 1.0, -2.0]))
+        use_bias = bool(rng.integers(2))
+        relu = bool(rng.integers(2))
+        yield i, path, out, M, N, K, alpha, beta, use_bias, relu
+
+
+@pytest.mark.parametrize("case", list(random_cases()), ids=lambda c: f"r{c[0]}")
+def test_random_shapes_epilogues_and_plans(case):
+    """Seeded random shapes, formats, epilogues; the workspace the best plan asks
+    for, so deep-K cases split and the rest do not."""
+    i, path, out, M, N, K, alpha, beta, use_bias, relu = case
+    p = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(out != "f32"))
+    print(f"case r{i} {path}->{out} {M}x{N}x{K} a={alpha} b={beta} bias={use_bias} relu={relu} "
+          f"plan {p}", flush=True)
+    rng = np.random.default_rng(6200 + i)
+    dtype = store(path)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    Cold = draw(rng, (M, N), "normal", out) if beta != 0.0 else None
+    bias = rng.standard_normal(N).astype(np.float32) if use_bias else None
+    C, ws = run_ex(path, out, A, B, alpha=alpha, beta=beta, Cold=Cold, bias=bias, relu=relu,
+                   ws_bytes=p["workspace_bytes"])
+    C64, S = oracle.gemm(dtype, A, B)
+    E, T = oracle.epilogue(C64, alpha, beta, None if Cold is None else oracle.widen(out, Cold),
+                           None if bias is None else bias.astype(np.float64), relu)
+    b = bound_epilogue(E, T, S, alpha, TOL_MFMA, out)
+    res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
+    assert res["ok"], res
+    assert gap_untouched(C) and spare_untouched(ws, p["workspace_bytes"])
