@@ -139,7 +139,7 @@ def test_tile_map_rejects_bad_arguments():
     (512, 512, "bf16", (128, 128)),       # 16 tiles instead of 4
     (2048, 2048, "f16", (128, 128)),      # 256 tiles instead of 64
     (4000, 3000, "f32", (128, 128)),      # 768 tiles (3 waves) beat 192 of 256^2
-    (4096, 4096, "f32", (256, 256)),
+    (4096, 4096, "f32", (128, 128)),      # fp32 prefers 128^2 (two workgroups per CU)
     (512, 512, "f32", (128, 128)),
     (4000, 3000, "f32x3", (256, 256)),    # the 3 x bf16 kernel has 256 x 256 only
     (512, 512, "f32x3", (256, 256)),
