@@ -14,6 +14,7 @@ the planner splits K, through gemm_ex with a workspace.
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
+                    [--no-power-clock] [--no-cold-cache]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -272,6 +273,7 @@ def main():
     ap.add_argument("--no-per-dtype", action="store_true")
     ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--no-power-clock", action="store_true")
+    ap.add_argument("--no-cold-cache", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -318,9 +320,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(value / peak, 4), "traffic": traffic},
     }
-    t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
-    line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
-                          "launches": 20, "how": "each launch after writing a 512 MiB buffer"}
+    if not args.no_cold_cache:
+        t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
+        line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
+                              "launches": 20, "how": "each launch after writing a 512 MiB buffer"}
     if not args.no_power_clock:
         print("bench: sampling clock and power under load", file=sys.stderr, flush=True)
         line["power_clock"] = power_clock(entry[args.dtype], Ad, Bd, Cd, per_launch, value, peak)
