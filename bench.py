@@ -10,7 +10,9 @@ fp32-input 4096^3 products are measured the same way and reported under
 after a 512 MiB write), and the graphics clock and socket power amd-smi reads
 while the product runs.  The other parity workloads, and one GPU's row share of the 4096^3
 product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
-the planner splits K, through gemm_ex with a workspace.
+the planner splits K, through gemm_ex with a workspace; each both launched call by
+call from Python and replayed from a HIP graph (the small shapes are otherwise
+bound by the host's launch rate).
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
@@ -223,6 +225,25 @@ SHAPES = [("f32 512^3", "f32_512", "f32"),
            ("bf16", 512, 4096, 4096), "bf16")]
 
 
+def time_graph(entry, Ad, Bd, Cd, launches: int):
+    """Mean time per call of `launches` calls captured in one HIP graph and
+    replayed: the kernels back to back, without the host's per-call launch cost."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            entry(Ad, Bd, Cd)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e-3 / launches
+
+
 def other_shapes(dg, args):
     """Per shape: the plain entry point, and gemm_ex with the workspace its
     split-K plan asks for when the plan splits."""
@@ -244,8 +265,10 @@ def other_shapes(dg, args):
         steps = max(10, min(args.steps, int(2e4 * 1e9 / flop_s)))
         warm = max(3, min(args.warmup, steps))
         t, _ = time_gemm(plain, Ad, Bd, Cd, steps, warm)
+        tg = time_graph(plain, Ad, Bd, Cd, min(steps, 100))
         rec = {"shape": label, "M": M, "N": N, "K": K, "steps": steps,
-               "plain_us": round(t * 1e6, 2), "plain_tflops": round(tflops(M, N, K, t), 2)}
+               "plain_us": round(t * 1e6, 2), "plain_tflops": round(tflops(M, N, K, t), 2),
+               "plain_graph_us": round(tg * 1e6, 2)}
         plan = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(Cd.dtype == Ad.dtype and
                                                                    path != "f32"))
         rec["plan"] = plan
@@ -255,8 +278,11 @@ def other_shapes(dg, args):
             def split_entry(a, b, c, stream=None, ws=ws):
                 dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
             t2, _ = time_gemm(split_entry, Ad, Bd, Cd, steps, warm)
+            t2g = time_graph(split_entry, Ad, Bd, Cd, min(steps, 100))
             rec["split_us"] = round(t2 * 1e6, 2)
             rec["split_tflops"] = round(tflops(M, N, K, t2), 2)
+            rec["split_graph_us"] = round(t2g * 1e6, 2)
+            rec["split_graph_tflops"] = round(tflops(M, N, K, t2g), 2)
             del ws
         out.append(rec)
         del Ad, Bd, Cd

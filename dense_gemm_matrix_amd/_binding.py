@@ -103,12 +103,33 @@ def _stream(C: torch.Tensor, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+class _on_device:
+    """Makes C's device current for the call (the library launches on the
+    current device), skipping torch's device switch when it already is."""
+    __slots__ = ("idx", "prev")
+
+    def __init__(self, t: torch.Tensor):
+        self.idx = t.device.index
+
+    def __enter__(self):
+        self.prev = torch.cuda.current_device()
+        if self.idx is not None and self.idx != self.prev:
+            torch.cuda.set_device(self.idx)
+        else:
+            self.prev = None
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def gemm_f32(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> None:
     """C = A @ B for fp32 A [M,K], B [K,N], C [M,N]; enqueued on `stream`."""
     M, N, K = _shapes(A, B, C)
     if not (A.dtype == B.dtype == C.dtype == torch.float32):
         raise TypeError("gemm_f32 takes float32 A, B and C")
-    with torch.cuda.device(C.device):
+    with _on_device(C):
         _check(_lib.gemm_f32(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(), _pitch(B, N),
                              C.data_ptr(), _pitch(C, N), _stream(C, stream)))
 
@@ -119,7 +140,7 @@ def gemm_f32_3xbf16(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=No
     M, N, K = _shapes(A, B, C)
     if not (A.dtype == B.dtype == C.dtype == torch.float32):
         raise TypeError("gemm_f32_3xbf16 takes float32 A, B and C")
-    with torch.cuda.device(C.device):
+    with _on_device(C):
         _check(_lib.gemm_f32_3xbf16(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(),
                                     _pitch(B, N), C.data_ptr(), _pitch(C, N), _stream(C, stream)))
 
@@ -134,7 +155,7 @@ def _gemm16(fn, dtype, A, B, C, stream):
         out = DGEMM_OUT_SAME
     else:
         raise TypeError(f"C must be float32 or {dtype}")
-    with torch.cuda.device(C.device):
+    with _on_device(C):
         _check(fn(M, N, K, A.data_ptr(), _pitch(A, K), B.data_ptr(), _pitch(B, N),
                   C.data_ptr(), _pitch(C, N), out, _stream(C, stream)))
 
@@ -190,7 +211,7 @@ def gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float =
         if workspace.device != C.device or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on C's device")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    with torch.cuda.device(C.device):
+    with _on_device(C):
         _check(_lib.gemm_ex(IN_CODES[fmt], out, M, N, K, A.data_ptr(), _pitch(A, K),
                             B.data_ptr(), _pitch(B, N), C.data_ptr(), _pitch(C, N),
                             float(alpha), float(beta), bias_ptr,

@@ -284,3 +284,41 @@ def test_random_shapes_epilogues_and_plans(case):
     res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
     assert res["ok"], res
     assert gap_untouched(C) and spare_untouched(ws, p["workspace_bytes"])
+
+
+@pytest.mark.parametrize("path,out,M,N,K", [("bf16", "bf16", 64, 72, 4104), ("f16", "f32", 300, 264, 200),
+                                            ("f32", "f32", 512, 512, 512)])
+def test_hip_graph_capture_replays_match_eager(path, out, M, N, K):
+    """gemm_ex (a split plan where the planner picks one) captured into a HIP
+    graph: every replay, with eager work on the same stream between replays,
+    reproduces the eager result bit for bit.  The library enqueues only kernel
+    launches (no memset, no allocation), which is what capture requires."""
+    p = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(out != "f32"))
+    print(f"case graph {path}->{out} {M}x{N}x{K} plan {p}", flush=True)
+    rng = np.random.default_rng(6300 + M)
+    dtype = store(path)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    Ad, Bd = dev_matrix(A, dtype), dev_matrix(B, dtype)
+    bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32)).to("cuda")
+    ws = torch.empty(max(p["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
+    ref = torch.empty((M, N), dtype=TORCH[out], device="cuda")
+    dg.gemm_ex(Ad, Bd, ref, bias=bias, relu=True, workspace=ws)
+    torch.cuda.synchronize()
+    C = torch.empty_like(ref)
+    other = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws)   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws)
+    for rep in range(4):
+        C.fill_(float("nan"))
+        g.replay()
+        dg.gemm_ex(Ad, Bd, other, workspace=ws)                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(C, ref), rep
