@@ -238,15 +238,19 @@ __device__ __forceinline__ int x3_off(int row, int chunk) {
 }
 
 // Split 8 fp32 values into packed hi and lo bf16 parts (element i in the low
-// half of word i / 2 when i is even).
+// half of word i / 2 when i is even).  Pairs go through one two-wide
+// conversion each (v_cvt_pk_bf16_f32, nearest even); hi widens back to fp32
+// exactly by placing its bits in the upper half of a word.
 __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const __bf16 h0 = (__bf16)x[2 * w], h1 = (__bf16)x[2 * w + 1];
-        const __bf16 l0 = (__bf16)(x[2 * w] - (float)h0);
-        const __bf16 l1 = (__bf16)(x[2 * w + 1] - (float)h1);
-        hi[w] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        lo[w] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        const f32x2 v = {x[2 * w], x[2 * w + 1]};
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const f32x2 hf = {as_float(h << 16), as_float(h & 0xffff0000u)};
+        hi[w] = h;
+        lo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
     }
 }
 
@@ -288,8 +292,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 
     // Global loads of step kt into registers.  Steps at or past the end get
     // empty ranges and load zeros (the schedule below issues them
-    // unconditionally; their data is never used).
-    auto load_step = [&](int kt) {
+    // unconditionally; their data is never used).  On the last step of a
+    // ragged K (`tail`), A's columns at or past K hold other data (row padding
+    // or the next row) and are zeroed, since the matching B rows are zero;
+    // that waits for the loads, once per call.
+    auto load_step = [&](int kt, bool tail) {
         const int k0 = kt * BK;
         const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
@@ -306,27 +313,26 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        if (tail) {
+            const int valid = K - k0 - ac * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[2 * i] = mask_tail32(ra[2 * i], valid);
+                ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
+            }
+        }
     };
 
-    // Store unit u (0..7) of step kt into stage s: u < 4 splits A row
-    // ar0 + 64 u (masking columns at or past K when `tail`: they hold other
-    // data, row padding or the next row, and must be exact zeros since the
-    // matching B rows are); u >= 4 splits column u - 4 of the B block (8
-    // consecutive k -> one chunk per part).
-    auto store_unit = [&](int s, int u, int kt, bool tail) {
+    // Store unit u (0..7) into stage s: u < 4 splits A row ar0 + 64 u; u >= 4
+    // splits column u - 4 of the B block (8 consecutive k -> one chunk per part).
+    auto store_unit = [&](int s, int u) {
         char* st = smem + s * X3_STAGE;
         float x[8];
         if (u < 4) {
-            u32x4 p0 = ra[2 * u], p1 = ra[2 * u + 1];
-            if (tail) {
-                const int valid = K - kt * BK - ac * 8;
-                p0 = mask_tail32(p0, valid);
-                p1 = mask_tail32(p1, valid - 4);
-            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = as_float(p0[e]);
-                x[4 + e] = as_float(p1[e]);
+                x[e] = as_float(ra[2 * u][e]);
+                x[4 + e] = as_float(ra[2 * u + 1][e]);
             }
         } else {
 #pragma unroll
@@ -391,30 +397,29 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     // runs in the shadow of the matrix instructions.  The last step also loads,
     // stores and reads "step nk" (zeros, inside the LDS array; never used).
     if (nk > 0) {
-        load_step(0);
+        load_step(0, ragged_k && nk == 1);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) store_unit(0, u, 0, ragged_k && nk == 1);
+        for (int u = 0; u < 8; ++u) store_unit(0, u);
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < 16; ++r) read_one(0, 0, fa[0], fb[0], r);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            const bool tail_next = ragged_k && kt + 2 == nk;
-            load_step(kt + 1);
+            load_step(kt + 1, ragged_k && kt + 2 == nk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 48; ++i) {
                 mfma_one(fa[0], fb[0], i);
                 __builtin_amdgcn_sched_barrier(0);
                 if (i < 16) read_one(cur, 1, fa[1], fb[1], i);
-                if (i >= 24 && (i - 24) % 6 == 0) store_unit(cur ^ 1, (i - 24) / 6, kt + 1, tail_next);
+                if (i >= 24 && (i - 24) % 6 == 0) store_unit(cur ^ 1, (i - 24) / 6);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int i = 0; i < 24; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i % 6 == 0) store_unit(cur ^ 1, 4 + i / 6, kt + 1, false);
+                if (i % 6 == 0) store_unit(cur ^ 1, 4 + i / 6);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
