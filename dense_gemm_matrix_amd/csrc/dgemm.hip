@@ -104,7 +104,7 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 struct TileCand { int bm, bn; double eff, pair; };
 constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0}, {192, 256, 0.95, 0.0}, {128, 128, 0.6, 1.26}};
 constexpr TileCand TILES32[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.85, 1.67}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.6, 1.22}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
 double rounds_factor(const TileCand& t, int64_t wgs) {
@@ -117,7 +117,7 @@ double rounds_factor(const TileCand& t, int64_t wgs) {
 const TileCand* tiles_for(int in, int& n) {
     if (in == IN_BF16 || in == IN_F16) { n = 3; return TILES16; }
     if (in == IN_F32) { n = 2; return TILES32; }
-    n = 1;
+    n = 2;
     return TILES32X3;
 }
 

@@ -229,23 +229,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
 // on the way, by its choice of which values to pack), so both operands are
 // read with ds_read_b128.  Double-buffered LDS, BK = 32.
 
-constexpr int X3_ROW = BK * 2;                  // 64-byte bf16 rows: 4 chunks
-constexpr int X3_PART = BM * X3_ROW;            // one part of one operand: 16 KiB
-constexpr int X3_STAGE = 4 * X3_PART;           // A hi, A lo, B hi, B lo: 64 KiB
+constexpr int X3_ROW = BK * 2;                  // 64-byte bf16 rows: 4 chunks of 8 k
 
 __device__ __forceinline__ int x3_off(int row, int chunk) {
     return row * X3_ROW + ((chunk ^ ((row ^ (row >> 2)) & 3)) << 4);
 }
 
-// Split 8 fp32 values into packed hi and lo bf16 parts (element i in the low
-// half of word i / 2 when i is even).  Pairs go through one two-wide
+// Split 2 W fp32 values into packed hi and lo bf16 parts (element i in the
+// low half of word i / 2 when i is even).  Pairs go through one two-wide
 // conversion each (v_cvt_pk_bf16_f32, nearest even); hi widens back to fp32
 // exactly by placing its bits in the upper half of a word.
-__device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+template <int W>
+__device__ __forceinline__ void split(const float (&x)[2 * W], uint32_t (&hi)[W], uint32_t (&lo)[W]) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < W; ++w) {
         const f32x2 v = {x[2 * w], x[2 * w + 1]};
         const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
         const f32x2 hf = {as_float(h << 16), as_float(h & 0xffff0000u)};
@@ -254,41 +253,53 @@ __device__ __forceinline__ void split8(const float (&x)[8], u32x4& hi, u32x4& lo
     }
 }
 
-template <bool EPI>
+// Square TB x TB macro-tile (256 or 128), 4 waves in a 2 x 2 layout, each
+// wave (TB/2)^2 = MI x MI blocks of 32 x 32 accumulators.  Staging per step
+// (BK = 32): A is TB rows, thread -> 8 consecutive k (two 16-byte fp32
+// pieces) of rows ar0 + 64 i (i < TB / 64); B is 32 k-rows x TB columns,
+// thread -> a KB k x 4 column block, KB = 8 at TB = 256 and 4 at TB = 128 (256
+// blocks either way).
+template <bool EPI, int TB>
 __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
     int kchunk, int64_t c_zstride, EpiArgs epi) {
+    static_assert(TB == 256 || TB == 128, "tile");
+    constexpr int MI = TB / 64;                  // 32 x 32 blocks per wave per dimension
+    constexpr int AR = TB / 64;                  // A rows per thread per step
+    constexpr int KB = TB == 256 ? 8 : 4;        // B k-rows per thread block
+    constexpr int PART = TB * X3_ROW;            // one part of one operand
+    constexpr int STAGE = 4 * PART;              // A hi, A lo, B hi, B lo
+    constexpr int NU = AR + 4;                   // store units per step
+    constexpr int NM = MI * MI * 3;              // MFMAs per chunk pair
+    constexpr int NR = 4 * MI;                   // fragment reads per chunk pair
     split_k_window(A, B, C, K, ldb, kchunk, c_zstride);
-    __shared__ __attribute__((aligned(1024))) char smem[2 * X3_STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
-    const int cols_b = (N - n0) < BN ? (N - n0) : BN;
+    const int m0 = tm * TB;
+    const int n0 = tn * TB;
+    const int rows_a = (M - m0) < TB ? (M - m0) : TB;
+    const int cols_b = (N - n0) < TB ? (N - n0) : TB;
     const int nk = (K + BK - 1) / BK;
     const bool ragged_k = (K % BK) != 0;
 
-    // A staging: thread -> 8 consecutive k (two 16-byte fp32 pieces) of rows
-    // ar0 + 64 i, i = 0..3, k chunk ac.
     const int ac = tid & 3;
     const int ar0 = tid >> 2;
-    // B staging: thread -> an 8 k x 4 column block (k rows 8 kb .., columns 4 nb ..).
-    const int kb = tid & 3;
-    const int nb = tid >> 2;
+    const int kb = tid % (BK / KB);
+    const int nb = tid / (BK / KB);
 
-    int voff_a[4], voff_b[8];
+    int voff_a[AR], voff_b[KB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) voff_a[i] = (ar0 + 64 * i) * lda * 4 + ac * 32;
+    for (int i = 0; i < AR; ++i) voff_a[i] = (ar0 + 64 * i) * lda * 4 + ac * 32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) voff_b[i] = (kb * 8 + i) * ldb * 4 + nb * 16;
+    for (int i = 0; i < KB; ++i) voff_b[i] = (kb * KB + i) * ldb * 4 + nb * 16;
 
-    u32x4 ra[8], rb[8];
+    u32x4 ra[2 * AR], rb[KB];
 
     // Global loads of step kt into registers.  Steps at or past the end get
     // empty ranges and load zeros (the schedule below issues them
@@ -307,43 +318,58 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < AR; ++i) {
             ra[2 * i] = load16(rsa, voff_a[i]);
             ra[2 * i + 1] = load16(rsa, voff_a[i] + 16);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rb[i] = load16(rsb, voff_b[i]);
+        for (int i = 0; i < KB; ++i) rb[i] = load16(rsb, voff_b[i]);
         if (tail) {
             const int valid = K - k0 - ac * 8;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < AR; ++i) {
                 ra[2 * i] = mask_tail32(ra[2 * i], valid);
                 ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
             }
         }
     };
 
-    // Store unit u (0..7) into stage s: u < 4 splits A row ar0 + 64 u; u >= 4
-    // splits column u - 4 of the B block (8 consecutive k -> one chunk per part).
+    // Store unit u (0 .. NU - 1) into stage s: u < AR splits A row ar0 + 64 u
+    // (8 k: one chunk per part); u >= AR splits column u - AR of the B block
+    // (KB k: one chunk per part at KB = 8, half a chunk at KB = 4).
     auto store_unit = [&](int s, int u) {
-        char* st = smem + s * X3_STAGE;
-        float x[8];
-        if (u < 4) {
+        char* st = smem + s * STAGE;
+        if (u < AR) {
+            float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 x[e] = as_float(ra[2 * u][e]);
                 x[4 + e] = as_float(ra[2 * u + 1][e]);
             }
+            uint32_t hi[4], lo[4];
+            split<4>(x, hi, lo);
+            const int off = x3_off(ar0 + 64 * u, ac);
+            *(u32x4*)(st + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            *(u32x4*)(st + PART + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
         } else {
+            const int cc = u - AR;
+            float x[KB];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = as_float(rb[e][u - 4]);
+            for (int e = 0; e < KB; ++e) x[e] = as_float(rb[e][cc]);
+            uint32_t hi[KB / 2], lo[KB / 2];
+            split<KB / 2>(x, hi, lo);
+            char* base = st + 2 * PART;
+            if constexpr (KB == 8) {
+                const int off = x3_off(nb * 4 + cc, kb);
+                *(u32x4*)(base + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *(u32x4*)(base + PART + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            } else {
+                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                const int off = x3_off(nb * 4 + cc, kb >> 1) + (kb & 1) * 8;
+                *(u32x2*)(base + off) = u32x2{hi[0], hi[1]};
+                *(u32x2*)(base + PART + off) = u32x2{lo[0], lo[1]};
+            }
         }
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        const int off = u < 4 ? x3_off(ar0 + 64 * u, ac) : x3_off(nb * 4 + (u - 4), kb);
-        char* base = st + (u < 4 ? 0 : 2 * X3_PART);
-        *(u32x4*)(base + off) = hi;
-        *(u32x4*)(base + X3_PART + off) = lo;
     };
 
     const int wm = wave >> 1;
@@ -351,34 +377,35 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     const int g = lane >> 5;
     const int li = lane & 31;
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][MI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
+        for (int nj = 0; nj < MI; ++nj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
     // Fragments of one 16-k chunk pair: [part][block], part 0 = hi, 1 = lo.
-    u32x4 fa[2][2][4], fb[2][2][4];
+    u32x4 fa[2][2][MI], fb[2][2][MI];
 
-    // Fragment read r (0..15) of pair kp from stage s: part r / 8; A block
-    // r % 8 when r % 8 < 4, else B block r % 8 - 4.
-    auto read_one = [&](int s, int kp, u32x4 (&a)[2][4], u32x4 (&b)[2][4], int r) {
-        const char* st = smem + s * X3_STAGE;
+    // Fragment read r (0 .. NR - 1) of pair kp from stage s: part r / (2 MI);
+    // A block q = r % (2 MI) when q < MI, else B block q - MI.
+    auto read_one = [&](int s, int kp, u32x4 (&a)[2][MI], u32x4 (&b)[2][MI], int r) {
+        const char* st = smem + s * STAGE;
         const int ch = 2 * kp + g;
-        const int p = r >> 3, q = r & 7;
-        if (q < 4)
-            a[p][q] = *(const u32x4*)(st + p * X3_PART + x3_off(wm * 128 + q * 32 + li, ch));
+        const int p = r / (2 * MI), q = r % (2 * MI);
+        if (q < MI)
+            a[p][q] = *(const u32x4*)(st + p * PART + x3_off(wm * (TB / 2) + q * 32 + li, ch));
         else
-            b[p][q - 4] = *(const u32x4*)(st + (2 + p) * X3_PART + x3_off(wn * 128 + (q - 4) * 32 + li, ch));
+            b[p][q - MI] =
+                *(const u32x4*)(st + (2 + p) * PART + x3_off(wn * (TB / 2) + (q - MI) * 32 + li, ch));
     };
 
-    // Matrix instruction i (0..47) of a pair: block i / 3 (mi, nj), product
-    // i % 3: the small terms first, then the leading one.
-    auto mfma_one = [&](const u32x4 (&a)[2][4], const u32x4 (&b)[2][4], int i) {
-        const int mi = (i / 3) >> 2, nj = (i / 3) & 3, t = i % 3;
-        const u32x4 av = t == 1 ? a[0][mi] : (t == 0 ? a[1][mi] : a[0][mi]);
+    // Matrix instruction i (0 .. NM - 1) of a pair: block i / 3 (mi, nj),
+    // product i % 3: the small terms first, then the leading one.
+    auto mfma_one = [&](const u32x4 (&a)[2][MI], const u32x4 (&b)[2][MI], int i) {
+        const int mi = (i / 3) / MI, nj = (i / 3) % MI, t = i % 3;
+        const u32x4 av = t == 0 ? a[1][mi] : a[0][mi];
         const u32x4 bv = t == 1 ? b[1][nj] : b[0][nj];
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[mi][nj], 0, 0, 0);
@@ -387,54 +414,62 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     // Schedule of step kt (stage cur holds it, stage cur ^ 1 receives step
     // kt + 1), in issue order; sched_barrier pins it:
     //   global loads of step kt + 1 into registers;
-    //   pair 0's 48 MFMAs, the first 16 each followed by one read of pair 1,
-    //   the last 24 by a store unit every 6 (A rows: split, write hi and lo);
-    //   pair 1's first 24 MFMAs, a store unit every 6 (B columns);
+    //   pair 0's NM MFMAs, the first NR each followed by one read of pair 1;
+    //   from the middle of pair 0 to the middle of pair 1, a store unit every
+    //   NM / NU MFMAs (A rows, then B columns: split, write hi and lo);
     //   barrier (stage cur ^ 1 complete; every read of stage cur issued);
-    //   pair 1's last 24 MFMAs, the first 16 each followed by one read of
-    //   step kt + 1's pair 0.
-    // The split and convert work (about 30 VALU instructions per unit) thus
-    // runs in the shadow of the matrix instructions.  The last step also loads,
-    // stores and reads "step nk" (zeros, inside the LDS array; never used).
+    //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0.
+    // The split and convert work thus runs in the shadow of the matrix
+    // instructions.  The last step also loads, stores and reads "step nk"
+    // (zeros, inside the LDS array; never used).
+    auto unit_at = [&](int slot) {  // store unit placed after MFMA slot (0 .. 2 NM - 1), or -1
+        const int d = slot - NM / 2;
+        return (d >= 0 && d % (NM / NU) == 0 && d / (NM / NU) < NU) ? d / (NM / NU) : -1;
+    };
+    static_assert(NM % NU == 0 || NM / NU >= 1, "unit spacing");
     if (nk > 0) {
         load_step(0, ragged_k && nk == 1);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) store_unit(0, u);
+        for (int u = 0; u < NU; ++u) store_unit(0, u);
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) read_one(0, 0, fa[0], fb[0], r);
+        for (int r = 0; r < NR; ++r) read_one(0, 0, fa[0], fb[0], r);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             load_step(kt + 1, ragged_k && kt + 2 == nk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 48; ++i) {
+            for (int i = 0; i < NM; ++i) {
                 mfma_one(fa[0], fb[0], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i < 16) read_one(cur, 1, fa[1], fb[1], i);
-                if (i >= 24 && (i - 24) % 6 == 0) store_unit(cur ^ 1, (i - 24) / 6);
+                if (i < NR) read_one(cur, 1, fa[1], fb[1], i);
+                if (unit_at(i) >= 0) store_unit(cur ^ 1, unit_at(i));
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int i = 0; i < 24; ++i) {
+            for (int i = 0; i < NM / 2; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i % 6 == 0) store_unit(cur ^ 1, 4 + i / 6);
+                if (unit_at(NM + i) >= 0) store_unit(cur ^ 1, unit_at(NM + i));
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
 #pragma unroll
-            for (int i = 24; i < 48; ++i) {
+            for (int i = NM / 2; i < NM; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i - 24 < 16) read_one(cur ^ 1, 0, fa[0], fb[0], i - 24);
+                constexpr int H = NM - NM / 2;
+                const int j = i - NM / 2;
+#pragma unroll
+                for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
+                    read_one(cur ^ 1, 0, fa[0], fb[0], r);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    store_tile<OUT_F32, 4, 4, EPI>(acc, C, M, N, ldc, m0 + wm * 128, n0 + wn * 128, g, li, epi,
-                                   m0 + BM <= M && n0 + BN <= N);
+    store_tile<OUT_F32, MI, MI, EPI>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
+                                     li, epi, m0 + TB <= M && n0 + TB <= N);
 }
 
 hipError_t go(const void* fn, const GemmLaunch& L) {
@@ -460,10 +495,12 @@ hipError_t launch_gemm32(const GemmLaunch& L) {
     if (L.in == IN_F32 && L.tbm == 128)
         return go(L.epi ? (const void*)gemm32_kernel<true, 128> : (const void*)gemm32_kernel<false, 128>,
                   L);
-    if (L.tbm != BM) return hipErrorInvalidValue;
-    if (L.in == IN_F32X3)
-        return go(L.epi ? (const void*)gemm32x3_kernel<true> : (const void*)gemm32x3_kernel<false>,
-                  L);
+    if (L.in == IN_F32X3 && L.tbm == 256)
+        return go(L.epi ? (const void*)gemm32x3_kernel<true, 256>
+                        : (const void*)gemm32x3_kernel<false, 256>, L);
+    if (L.in == IN_F32X3 && L.tbm == 128)
+        return go(L.epi ? (const void*)gemm32x3_kernel<true, 128>
+                        : (const void*)gemm32x3_kernel<false, 128>, L);
     return hipErrorInvalidValue;
 }
 

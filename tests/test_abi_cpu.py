@@ -141,8 +141,8 @@ def test_tile_map_rejects_bad_arguments():
     (4000, 3000, "f32", (128, 128)),      # 768 tiles (3 waves) beat 192 of 256^2
     (4096, 4096, "f32", (128, 128)),      # fp32 prefers 128^2 (two workgroups per CU)
     (512, 512, "f32", (128, 128)),
-    (4000, 3000, "f32x3", (256, 256)),    # the 3 x bf16 kernel has 256 x 256 only
-    (512, 512, "f32x3", (256, 256)),
+    (4000, 3000, "f32x3", (256, 256)),
+    (512, 512, "f32x3", (128, 128)),
 ])
 def test_tile_choice(M, N, fmt, tile):
     info = dg.dgemm_tile_map(M, N, fmt)
@@ -242,7 +242,7 @@ from hypothesis import given, settings, strategies as st  # noqa: E402
 def test_plan_invariants(M, N, K, fmt, ws):
     p = dg.gemm_ex_plan(fmt, M, N, K, ws)
     tiles = {"f32": {(256, 256), (128, 128)}, "bf16": {(256, 256), (192, 256), (128, 128)},
-             "f16": {(256, 256), (192, 256), (128, 128)}, "f32x3": {(256, 256)}}[fmt]
+             "f16": {(256, 256), (192, 256), (128, 128)}, "f32x3": {(256, 256), (128, 128)}}[fmt]
     assert (p["tile_rows"], p["tile_cols"]) in tiles
     assert 1 <= p["splits"] <= 16
     assert p["workspace_bytes"] <= ws
