@@ -2,22 +2,21 @@
 //
 //   * gemm32_kernel: gfx950 has no reduced-precision (xf32) matrix
 //     instruction, so products use full-precision v_mfma_f32_32x32x2_f32.
-//     Operands are staged through registers (B's 8 x 4 fp32 blocks are
+//     Operands are staged through registers (B's k x 4 fp32 blocks are
 //     transposed by register renaming), double-buffered in LDS with BK = 32.
 //   * gemm32x3_kernel: the same data on bf16 matrix instructions, each input
 //     split in two bf16 parts and three products taken per term.
 //
-// Workgroup layout, tile map, swizzle principle, edge handling and epilogue as
-// in the 16-bit kernel: 256 x 256 macro-tile, 4 waves in a 2 x 2 layout, each
-// wave 128 x 128 as 4 x 4 blocks of 32 x 32 fp32 accumulators.
+// Both are templates over a square macro-tile of 256 or 128 (128 x 128 uses
+// 64 KiB of LDS, so two workgroups share a CU).  Workgroup layout, tile map,
+// swizzle principle, edge handling and epilogue as in the 16-bit kernel: 4
+// waves in a 2 x 2 layout, each wave (TB/2)^2 as blocks of 32 x 32 fp32
+// accumulators.
 
 #include "kern_common.h"
 
 namespace dgemm {
 namespace {
-
-constexpr int BM = 256;                       // macro-tile rows
-constexpr int BN = 256;                       // macro-tile columns
 constexpr int BK = 32;                        // K per step (fp32: 128-byte LDS rows)
 
 // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
