@@ -258,12 +258,15 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
     // Schedule (S16 stages, KP16 chunk pairs per step), written out in issue
     // order: with one wave per SIMD nothing else hides a stall, so every
     // load and LDS read sits between two MFMAs (sched_barrier pins the order).
-    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: during pair 0's MFMAs
-    // read the fragments of pairs 1 .. KP16 - 1 (one register set per pair);
-    // then wait until step kt + 1 has landed (later steps may still be in
-    // flight) and barrier, which retires every wave's reads of stage kt % S16;
-    // then, spread over the MFMAs of pairs 1 .. KP16 - 1, refill that stage
-    // with step kt + S16, and during the last pair read pair 0 of step kt + 1.
+    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: spread over the MFMAs
+    // of pairs 0 and 1, read the fragments of pairs 1 .. KP16 - 1 (one
+    // register set per pair; each pair's reads are issued before its MFMAs
+    // start); then wait until step kt + 1 has landed (later steps may still be
+    // in flight) and barrier, which retires every wave's reads of stage
+    // kt % S16; then, spread over the MFMAs of pairs 2 .. KP16 - 1, refill that
+    // stage with step kt + S16, and during the last pair read pair 0 of step
+    // kt + 1.  (A barrier after pair 0, with the refill over three pairs,
+    // measured about 1 % slower.)
     // The last step reads that pair too (from the stage the empty loads past
     // K have zero-filled, inside the LDS array; the registers are never
     // used): an unconditional read saves a branch per matrix instruction.
@@ -276,11 +279,12 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
         for (int kt = 0; kt < nk; ++kt) {
             constexpr int NR = T::NREAD * (KP16 - 1);
 #pragma unroll
-            for (int i = 0; i < T::NMFMA; ++i) {
-                mfma_one(fa[0], fb[0], i / NJ, i % NJ);
+            for (int i = 0; i < 2 * T::NMFMA; ++i) {
+                if (i < T::NMFMA) mfma_one(fa[0], fb[0], i / NJ, i % NJ);
+                else mfma_one(fa[1], fb[1], (i - T::NMFMA) / NJ, (i - T::NMFMA) % NJ);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int r = (i * NR) / T::NMFMA; r < ((i + 1) * NR) / T::NMFMA; ++r)
+                for (int r = (i * NR) / (2 * T::NMFMA); r < ((i + 1) * NR) / (2 * T::NMFMA); ++r)
                     read_piece(kt, 1 + r / T::NREAD, fa[1 + r / T::NREAD], fb[1 + r / T::NREAD],
                                r % T::NREAD);
                 __builtin_amdgcn_sched_barrier(0);
@@ -290,14 +294,14 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
             const StageDesc d = stage_desc(kt + S16);
             sync(TwoStepsLeft{});
             if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            constexpr int SLOTS = T::NMFMA * (KP16 - 1);
+            constexpr int SLOTS = T::NMFMA * (KP16 - 2);
 #pragma unroll
-            for (int kp = 1; kp < KP16; ++kp) {
+            for (int kp = 2; kp < KP16; ++kp) {
 #pragma unroll
                 for (int i = 0; i < T::NMFMA; ++i) {
                     mfma_one(fa[kp], fb[kp], i / NJ, i % NJ);
                     __builtin_amdgcn_sched_barrier(0);
-                    const int slot = (kp - 1) * T::NMFMA + i;
+                    const int slot = (kp - 2) * T::NMFMA + i;
 #pragma unroll
                     for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
                         dma_one(d, j);
