@@ -13,6 +13,7 @@ import dense_gemm_matrix_amd as dg
 import oracle
 from oracle.parity import TOL_MFMA
 from synth_inputs import draw, pair, workload
+from synth_inputs import to_torch as TORCH_FROM
 from tests.gpu_util import TORCH, dev_matrix, gap_untouched, round_pitch, sentinel_c, to64
 
 pytestmark = pytest.mark.gpu
@@ -225,3 +226,43 @@ def test_invalid_arguments_leave_c_untouched():
     torch.cuda.synchronize()
     C64, S = oracle.gemm("bf16", A, B)
     assert oracle.check(to64(C), C64, S, TOL_MFMA, "f32")["ok"]
+
+
+def test_leading_dimensions_at_the_32_bit_descriptor_limit():
+    """A's row pitch just under the largest a 256-row panel allows (256 lda 2 B
+    < 2 GiB) and B's just under the largest a 64-row K step allows (128 ldb B
+    < 2 GiB): the kernel's 32-bit buffer offsets reach ~2.14e9 bytes.  Each
+    operand then spans about 2.1 GB of device memory."""
+    M, N, K = 256, 64, 64
+    lda = (1 << 31) // (256 * 2) - 8
+    ldb = (1 << 31) // 128 - 8
+    A, B = pair(M, N, K, "normal", "bf16", seed=7000)
+    Abuf = torch.empty(((M - 1) * lda + K,), dtype=torch.bfloat16, device="cuda")
+    Bbuf = torch.empty(((K - 1) * ldb + N,), dtype=torch.bfloat16, device="cuda")
+    Ad = torch.as_strided(Abuf, (M, K), (lda, 1))
+    Bd = torch.as_strided(Bbuf, (K, N), (ldb, 1))
+    Ad.copy_(TORCH_FROM(A, "bf16"))
+    Bd.copy_(TORCH_FROM(B, "bf16"))
+    C = sentinel_c(M, N, "f32")
+    dg.gemm_bf16(Ad, Bd, C)
+    torch.cuda.synchronize()
+    C64, S = oracle.gemm("bf16", A, B)
+    assert oracle.check(to64(C), C64, S, TOL_MFMA, "f32")["ok"]
+    assert gap_untouched(C)
+    del Abuf, Bbuf
+
+
+def test_output_beyond_2_31_elements():
+    """C with 70000 x 32768 > 2^31 elements (4.6 GB of bf16): the epilogue's
+    64-bit element offsets; rows at both ends checked against the oracle."""
+    M, N, K = 70000, 32768, 64
+    A, B = pair(M, N, K, "ints", "bf16", seed=7100)
+    Ad, Bd = dev_matrix(A, "bf16", K), dev_matrix(B, "bf16", N)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.gemm_bf16(Ad, Bd, C)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 65535, 65536, 65537, M - 257, M - 256, M - 2, M - 1])
+    C64, _ = oracle.gemm("bf16", A, B, rows=rows)
+    got = to64(C[torch.from_numpy(rows).to("cuda")])
+    assert np.array_equal(got, oracle.widen("bf16", oracle.round_to("bf16", C64)))
+    del C
