@@ -325,6 +325,9 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
     per_launch, wall = time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, args.warmup)
+    # Five more timed blocks of the same K steps (no further warm-up), for the
+    # spread between trials; `value` stays the first block's.
+    trials = [time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, 0)[0] for _ in range(5)]
     value = tflops(M, N, K, per_launch)
     peak = PEAK_TFLOPS[args.dtype]
     traffic = measured_traffic(name)
@@ -342,7 +345,10 @@ def main():
         "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": DESCRIPTION[name], "M": M, "N": N, "K": K,
-                   "frac_of_peak": round(value / peak, 4), "wall_s_timed_region": round(wall, 4)},
+                   "frac_of_peak": round(value / peak, 4), "wall_s_timed_region": round(wall, 4),
+                   "trials_ms_per_step": [round(t * 1e3, 5) for t in trials],
+                   "trials_median_ms": round(sorted(trials)[2] * 1e3, 5),
+                   "trials_min_ms": round(min(trials) * 1e3, 5)},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(value / peak, 4), "traffic": traffic},
     }

@@ -121,3 +121,33 @@ def test_bound_accepts_gpu_arithmetic_and_rejects_planted_errors(out):
     pushed = E.copy()
     pushed[3, 4] += 1.01 * b[3, 4] * (1 if E[3, 4] >= 0 else -1)
     assert not check(pushed, E, S, TOL_MFMA, out, b=b)["ok"]
+
+
+# ---------------------------------------------------------------- the 3 x bf16 split's error
+
+def _bf16_rne(x64):
+    return oracle.widen("bf16", oracle.round_to("bf16", x64))
+
+
+def test_three_product_bf16_split_error_bound():
+    """The fp32-via-3xbf16 path takes x = hi + lo with hi = bf16(x), lo =
+    bf16(x - hi) (nearest even; x - hi is exact in fp32) and a*b as
+    ah*bh + ah*bl + al*bh.  Each term is exact in fp32 (8 x 8 significant bits),
+    so per product the error is the dropped al*bl plus the two lo truncations:
+    at most about 3 * 2^-16 |a b|.  The parity tolerance of that path (1e-4 S)
+    rests on this; checked here on random fp32 values and on values built to
+    make lo as large as possible."""
+    rng = np.random.default_rng(8000)
+    a = rng.standard_normal(200000).astype(np.float32).astype(np.float64)
+    b = (rng.standard_normal(200000) * 1e3).astype(np.float32).astype(np.float64)
+    # worst cases: mantissas whose low 16 bits sit just below a bf16 rounding tie
+    worst = np.array([1.0 + 2.0 ** -8 - 2.0 ** -23, 1.0 + 2.0 ** -9 - 2.0 ** -23, 1.99609363079071])
+    a = np.concatenate([a, worst, -worst])
+    b = np.concatenate([b, worst[::-1], worst])
+    ah, bh = _bf16_rne(a), _bf16_rne(b)
+    al, bl = _bf16_rne(a - ah), _bf16_rne(b - bh)
+    approx = ah * bh + ah * bl + al * bh
+    rel = np.abs(approx - a * b) / np.abs(a * b)
+    assert rel.max() <= 3 * 2.0 ** -16
+    # and the split is not exact, so the bound is not vacuous
+    assert rel.max() > 2.0 ** -20
