@@ -134,14 +134,82 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[MI][NJ], cha
     }
 }
 
+// Two fp32 values rounded to nearest even in C's 16-bit format, `lo` in the
+// low half of the word.
+template <int OUT>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    if constexpr (OUT == OUT_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// DPP quad permutation [1, 0, 3, 2]: lane l reads lane l ^ 1.
+constexpr int DPP_QUAD_XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_QUAD_XOR1, 0xf, 0xf, false);
+}
+
+// Epilogue for 16-bit C on a tile that lies wholly inside C.  In the 32x32
+// layout an even lane l and lane l + 1 hold columns c and c + 1; registers r
+// and r + 1 (r even) hold rows R and R + 1.  Each lane rounds its two values
+// into one word; one exchange between the two lanes then gives the even lane
+// row R, columns c .. c + 1, and the odd lane row R + 1, the same columns: one
+// 4-byte store where the per-element form needs two 2-byte ones, and each
+// half-wave store writes two 64-byte row pieces instead of one.  The epilogue
+// and the rounding act on each value before the exchange, so the stored values
+// are those of store_tile_impl.  Needs every lane of the wave active.
+template <int OUT, int MI, int NJ, bool EPI>
+__device__ __forceinline__ void store_tile16_full(const f32x16 (&acc)[MI][NJ], char* C, int ldc,
+                                                  int row0, int col0, int g, int li,
+                                                  const EpiArgs& e) {
+    const int odd = li & 1;
+    // v_perm_b32 takes bytes 0-3 from its second source and 4-7 from its first:
+    // the even lane keeps its low half (row R) and takes the neighbour's; the odd
+    // lane takes the neighbour's high half (row R + 1) and keeps its own.
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) {
+            const int col = col0 + nj * 32 + li;
+            float bias = 0.0f;
+            if (EPI && e.bias) bias = e.bias[col];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                float v0 = acc[mi][nj][r];
+                float v1 = acc[mi][nj][r + 1];
+                if constexpr (EPI) {
+                    v0 = epilogue<OUT>(v0, C, (int64_t)row * ldc + col, bias, e);
+                    v1 = epilogue<OUT>(v1, C, (int64_t)(row + 1) * ldc + col, bias, e);
+                }
+                const uint32_t p = pack16<OUT>(v0, v1);
+                const uint32_t w = __builtin_amdgcn_perm(swap_adjacent_lanes(p), p, sel);
+                const int64_t idx = (int64_t)(row + odd) * ldc + (col - odd);
+                *reinterpret_cast<uint32_t*>(C + idx * 2) = w;
+            }
+        }
+    }
+}
+
 template <int OUT, int MI, int NJ, bool EPI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
                                            int ldc, int row0, int col0, int g, int li,
                                            const EpiArgs& e, bool full) {
-    if (full)
-        store_tile_impl<OUT, MI, NJ, EPI, true>(acc, C, M, N, ldc, row0, col0, g, li, e);
-    else
+    if (full) {
+        if constexpr (OUT == OUT_F32)
+            store_tile_impl<OUT, MI, NJ, EPI, true>(acc, C, M, N, ldc, row0, col0, g, li, e);
+        else
+            store_tile16_full<OUT, MI, NJ, EPI>(acc, C, ldc, row0, col0, g, li, e);
+    } else {
         store_tile_impl<OUT, MI, NJ, EPI, false>(acc, C, M, N, ldc, row0, col0, g, li, e);
+    }
 }
 
 }  // namespace dgemm
