@@ -78,7 +78,7 @@ def measured_traffic(workload: str):
     if fields.get("kernel_source_sha256") != kernel_source_sha():
         return None
     v = fields.get(f"{workload}_hbm_bytes_per_launch")
-    return float(v) if v else None
+    return int(v) if v else None
 
 
 def device_inputs(name):
@@ -172,36 +172,82 @@ def cold_cache(entry, Ad, Bd, Cd, launches: int = 20):
     return total / launches
 
 
-def power_clock(entry, Ad, Bd, Cd, per_launch_s: float, value_tflops: float, peak: float):
-    """Graphics clock and socket power while the GEMM runs: about 1.5 s of
-    launches are queued, amd-smi (a child process) samples the device, then the
-    queue drains.  None when amd-smi is missing or fails."""
+def power_clock(entry, Ad, Bd, Cd, per_launch_s: float, value_tflops: float, peak: float,
+                samples: int = 5):
+    """Graphics clock and socket power while the GEMM runs.  This process keeps
+    the GPU busy with blocks of ~20 ms of launches, never more than three blocks
+    ahead, for 1 s before the first sample and 0.5 s between samples (amd-smi's
+    readings trail the load), and while amd-smi (a child process) runs, `samples`
+    times in turn.  The readings swing under the power limit, hence the list and
+    its mean.  None when amd-smi is missing or fails."""
     import subprocess
     import torch
-    n = int(min(50000, max(1000, 1.5 / max(per_launch_s, 1e-6))))
     stream = torch.cuda.current_stream()
-    for _ in range(n):
-        entry(Ad, Bd, Cd, stream=stream)
-    try:
-        raw = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"],
-                             capture_output=True, text=True, timeout=60).stdout
-        data = json.loads(raw)
-    except Exception:  # noqa: BLE001 - any failure means "not measured"
-        data = None
+    block = int(min(2000, max(20, 0.02 / max(per_launch_s, 1e-6))))
+
+    def queue_block():
+        for _ in range(block):
+            entry(Ad, Bd, Cd, stream=stream)
+        done = torch.cuda.Event()
+        done.record(stream)
+        return done
+
+    pending = []
+
+    def keep_busy(until):
+        """Queue blocks until `until()` is true, at most three blocks ahead."""
+        n = 0
+        while not until():
+            pending.append(queue_block())
+            n += block
+            while len(pending) > 3:
+                pending.pop(0).synchronize()
+        return n
+
+    def for_seconds(sec):
+        end = time.perf_counter() + sec
+        return lambda: time.perf_counter() >= end
+
+    launches = keep_busy(for_seconds(1.0))
+    clks, powers = [], []
+    for i in range(samples):
+        if i:
+            launches += keep_busy(for_seconds(0.5))
+        try:
+            proc = subprocess.Popen(["amd-smi", "metric", "--clock", "--power", "--json"],
+                                    stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            break
+        deadline = time.perf_counter() + 60.0
+        launches += keep_busy(lambda: proc.poll() is not None or time.perf_counter() >= deadline)
+        if proc.poll() is None:
+            proc.kill()
+        out = proc.communicate()[0]
+        # The last block still queued or running: the GPU was busy throughout.
+        if proc.returncode != 0 or pending[-1].query():
+            break
+        try:
+            data = json.loads(out)
+        except ValueError:
+            break
+        c = _smi_values(data, "gfx_")
+        if not c:
+            break
+        clks.append(sum(c) / len(c))
+        pw = _smi_values(data, "socket_power")
+        if pw:
+            powers.append(pw[0])
     torch.cuda.synchronize()
-    if data is None:
-        return None
-    clks = _smi_values(data, "gfx_")
-    power = _smi_values(data, "socket_power")
     if not clks:
         return None
     sclk = sum(clks) / len(clks)
     adj_peak = peak * sclk / 2400.0
-    return {"sclk_mhz_mean": round(sclk, 1), "sclk_mhz_per_xcd": clks,
-            "socket_power_w": power[0] if power else None,
+    return {"sclk_mhz_mean": round(sclk, 1), "sclk_mhz_samples": [round(c, 1) for c in clks],
+            "socket_power_w_samples": powers,
             "clock_adjusted_peak_tflops": round(adj_peak, 1),
             "frac_of_clock_adjusted_peak": round(value_tflops / adj_peak, 4),
-            "how": f"amd-smi sampled once while {n} queued launches ran"}
+            "how": f"{len(clks)} amd-smi samples (mean over the XCDs each) taken while the GPU "
+                   f"ran {launches} launches back to back"}
 
 
 def copy_calibration(gib: float = 1.0, reps: int = 5):

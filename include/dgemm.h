@@ -85,6 +85,9 @@ int gemm_f32(int M, int N, int K,
  * within 1e-4 * sum_k |a_ik * b_kj| of the exact product.  This is the
  * MI355X counterpart of the sgemm tf32 page's approach (fp32 data on
  * reduced-precision tensor units), more accurate than TF32's 10-bit inputs.
+ * Non-finite inputs: a NaN propagates as in gemm_f32, but an infinite x has
+ * lo = inf - inf = NaN, so the outputs it reaches are NaN, not infinite (as
+ * are those of finite inputs too large for bf16, |x| >= (2 - 2^-8) * 2^127).
  * Arguments, layout, errors and execution as gemm_f32.
  */
 int gemm_f32_3xbf16(int M, int N, int K,
