@@ -224,11 +224,17 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, *, bias: torch.Tens
            stream=None) -> torch.Tensor:
     """Allocates C (torch allocator) and computes C = act(alpha * A @ B + bias).
 
-    With split_k, the workspace a split-K plan asks for is taken from torch's
-    allocator on the same stream (it is free again once the kernels that use it
-    have run, in stream order)."""
+    C and, with split_k, the workspace a split-K plan asks for are taken from
+    torch's allocator on the stream the kernels run on (`stream`, else the
+    current one).  The workspace is released on return; the allocator hands
+    that block out again only to later work on the same stream, which runs after
+    these kernels.  C belongs to that stream too: a caller that goes on to use
+    it on another stream orders the two streams (or calls C.record_stream)."""
     if out_dtype is None:
         out_dtype = A.dtype
+    if stream is not None and stream != torch.cuda.current_stream(A.device):
+        with torch.cuda.stream(stream):
+            return matmul(A, B, out_dtype, bias=bias, relu=relu, alpha=alpha, split_k=split_k)
     C = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype, device=A.device)
     ws = None
     if split_k:
@@ -237,7 +243,7 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, *, bias: torch.Tens
                             out_same=(out_dtype == A.dtype and fmt != "f32"))
         if plan["splits"] > 1:
             ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=A.device)
-    gemm_ex(A, B, C, alpha=alpha, bias=bias, relu=relu, workspace=ws, stream=stream)
+    gemm_ex(A, B, C, alpha=alpha, bias=bias, relu=relu, workspace=ws)
     return C
 
 
