@@ -234,22 +234,18 @@ __device__ __forceinline__ int x3_off(int row, int chunk) {
     return row * X3_ROW + ((chunk ^ ((row ^ (row >> 2)) & 3)) << 4);
 }
 
-// Split 2 W fp32 values into packed hi and lo bf16 parts (element i in the
-// low half of word i / 2 when i is even).  Pairs go through one two-wide
-// conversion each (v_cvt_pk_bf16_f32, nearest even); hi widens back to fp32
-// exactly by placing its bits in the upper half of a word.
-template <int W>
-__device__ __forceinline__ void split(const float (&x)[2 * W], uint32_t (&hi)[W], uint32_t (&lo)[W]) {
+// Split two fp32 values into packed hi and lo bf16 parts (x0 in the low half
+// of each word).  One two-wide conversion per part (v_cvt_pk_bf16_f32, nearest
+// even); hi widens back to fp32 exactly by placing its bits in the upper half
+// of a word.  Six VALU instructions.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-        const f32x2 v = {x[2 * w], x[2 * w + 1]};
-        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-        const f32x2 hf = {as_float(h << 16), as_float(h & 0xffff0000u)};
-        hi[w] = h;
-        lo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
-    }
+    const f32x2 v = {x0, x1};
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 hf = {as_float(h << 16), as_float(h & 0xffff0000u)};
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
 }
 
 // Square TB x TB macro-tile (256 or 128), 4 waves in a 2 x 2 layout, each
@@ -303,72 +299,108 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     // Global loads of step kt into registers.  Steps at or past the end get
     // empty ranges and load zeros (the schedule below issues them
     // unconditionally; their data is never used).  On the last step of a
-    // ragged K (`tail`), A's columns at or past K hold other data (row padding
-    // or the next row) and are zeroed, since the matching B rows are zero;
-    // that waits for the loads, once per call.
-    auto load_step = [&](int kt, bool tail) {
+    // ragged K, A's columns at or past K hold other data (row padding or the
+    // next row) and are zeroed (mask_a), since the matching B rows are zero;
+    // that waits for the loads, once per call.  step_desc makes the step's two
+    // resources; load_one issues load j (0 .. NLOAD - 1, A's first), so that
+    // the main loop can spread them over matrix instructions.
+    constexpr int NLOAD = 2 * AR + KB;
+    struct StepDesc {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto step_desc = [&](int kt) {
         const int k0 = kt * BK;
         const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
         const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 4 : 0;
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
         const int rows_b = krem < BK ? krem : BK;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+        return StepDesc{make_rsrc(abase, abytes), make_rsrc(bbase, bbytes)};
+    };
+    auto load_one = [&](const StepDesc& d, int j) {
+        if (j < 2 * AR)
+            ra[j] = load16(d.a, voff_a[j >> 1] + (j & 1) * 16);
+        else
+            rb[j - 2 * AR] = load16(d.b, voff_b[j - 2 * AR]);
+    };
+    auto mask_a = [&](int kt) {
+        const int valid = K - kt * BK - ac * 8;
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
-            ra[2 * i] = load16(rsa, voff_a[i]);
-            ra[2 * i + 1] = load16(rsa, voff_a[i] + 16);
+            ra[2 * i] = mask_tail32(ra[2 * i], valid);
+            ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
         }
+    };
+    auto load_step = [&](int kt, bool tail) {
+        const StepDesc d = step_desc(kt);
 #pragma unroll
-        for (int i = 0; i < KB; ++i) rb[i] = load16(rsb, voff_b[i]);
-        if (tail) {
-            const int valid = K - k0 - ac * 8;
-#pragma unroll
-            for (int i = 0; i < AR; ++i) {
-                ra[2 * i] = mask_tail32(ra[2 * i], valid);
-                ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
-            }
-        }
+        for (int j = 0; j < NLOAD; ++j) load_one(d, j);
+        if (tail) mask_a(kt);
     };
 
     // Store unit u (0 .. NU - 1) into stage s: u < AR splits A row ar0 + 64 u
     // (8 k: one chunk per part); u >= AR splits column u - AR of the B block
-    // (KB k: one chunk per part at KB = 8, half a chunk at KB = 4).
-    auto store_unit = [&](int s, int u) {
+    // (KB k: one chunk per part at KB = 8, half a chunk at KB = 4).  A unit is
+    // done in pieces so that its work can be spread over several matrix
+    // instructions: piece w < unit_pairs(u) splits value pair w into uh[w],
+    // ul[w]; the last piece writes both parts to LDS.
+    uint32_t uh[4], ul[4];
+    auto unit_pairs = [](int u) { return u < AR ? 4 : KB / 2; };
+    auto unit_piece = [&](int s, int u, int w) __attribute__((always_inline)) {
+        if (w < unit_pairs(u)) {
+            float x0, x1;
+            if (u < AR) {
+                const u32x4& r = ra[2 * u + (w >> 1)];
+                x0 = as_float(r[(w & 1) * 2]);
+                x1 = as_float(r[(w & 1) * 2 + 1]);
+            } else {
+                x0 = as_float(rb[2 * w][u - AR]);
+                x1 = as_float(rb[2 * w + 1][u - AR]);
+            }
+            // Empty volatile asm statements pin the split to this point of the
+            // schedule: the instruction selector orders them with the
+            // sched_barriers, which pure arithmetic alone does not follow.
+            asm volatile("" : "+v"(x0), "+v"(x1));
+            split_pair(x0, x1, uh[w], ul[w]);
+            asm volatile("" ::"v"(uh[w]), "v"(ul[w]));
+            return;
+        }
         char* st = smem + s * STAGE;
         if (u < AR) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = as_float(ra[2 * u][e]);
-                x[4 + e] = as_float(ra[2 * u + 1][e]);
-            }
-            uint32_t hi[4], lo[4];
-            split<4>(x, hi, lo);
             const int off = x3_off(ar0 + 64 * u, ac);
-            *(u32x4*)(st + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-            *(u32x4*)(st + PART + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            *(u32x4*)(st + off) = u32x4{uh[0], uh[1], uh[2], uh[3]};
+            *(u32x4*)(st + PART + off) = u32x4{ul[0], ul[1], ul[2], ul[3]};
         } else {
             const int cc = u - AR;
-            float x[KB];
-#pragma unroll
-            for (int e = 0; e < KB; ++e) x[e] = as_float(rb[e][cc]);
-            uint32_t hi[KB / 2], lo[KB / 2];
-            split<KB / 2>(x, hi, lo);
             char* base = st + 2 * PART;
             if constexpr (KB == 8) {
                 const int off = x3_off(nb * 4 + cc, kb);
-                *(u32x4*)(base + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-                *(u32x4*)(base + PART + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+                *(u32x4*)(base + off) = u32x4{uh[0], uh[1], uh[2], uh[3]};
+                *(u32x4*)(base + PART + off) = u32x4{ul[0], ul[1], ul[2], ul[3]};
             } else {
                 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
                 const int off = x3_off(nb * 4 + cc, kb >> 1) + (kb & 1) * 8;
-                *(u32x2*)(base + off) = u32x2{hi[0], hi[1]};
-                *(u32x2*)(base + PART + off) = u32x2{lo[0], lo[1]};
+                *(u32x2*)(base + off) = u32x2{uh[0], uh[1]};
+                *(u32x2*)(base + PART + off) = u32x2{ul[0], ul[1]};
             }
         }
+    };
+    // Pieces in order: unit 0's pairs and write, unit 1's, ...
+    constexpr int NPIECE = AR * 5 + 4 * (KB / 2 + 1);
+    auto store_pieces = [&](int s, int p0, int p1) __attribute__((always_inline)) {  // pieces [p0, p1)
+#pragma unroll
+        for (int p = p0; p < p1; ++p) {
+            constexpr int PB = KB / 2 + 1;  // pieces per B unit
+            if (p < AR * 5)
+                unit_piece(s, p / 5, p % 5);
+            else
+                unit_piece(s, AR + (p - AR * 5) / PB, (p - AR * 5) % PB);
+        }
+    };
+    auto store_unit = [&](int s, int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int w = 0; w <= unit_pairs(u); ++w) unit_piece(s, u, w);
     };
 
     const int wm = wave >> 1;
@@ -412,20 +444,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 
     // Schedule of step kt (stage cur holds it, stage cur ^ 1 receives step
     // kt + 1), in issue order; sched_barrier pins it:
-    //   global loads of step kt + 1 into registers;
-    //   pair 0's NM MFMAs, the first NR each followed by one read of pair 1;
-    //   from the middle of pair 0 to the middle of pair 1, a store unit every
-    //   NM / NU MFMAs (A rows, then B columns: split, write hi and lo);
+    //   pair 0's NM MFMAs, the first NR each followed by one read of pair 1
+    //   and the first NLOAD by one global load of step kt + 1;
+    //   from the middle of pair 0 to the middle of pair 1 (NM MFMA slots), the
+    //   NPIECE store pieces, spread evenly: at 256 x 256 one or two per slot,
+    //   six VALU instructions or two LDS writes, few enough to issue while
+    //   the matrix instruction before them runs;
     //   barrier (stage cur ^ 1 complete; every read of stage cur issued);
     //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0.
-    // The split and convert work thus runs in the shadow of the matrix
-    // instructions.  The last step also loads, stores and reads "step nk"
-    // (zeros, inside the LDS array; never used).
-    auto unit_at = [&](int slot) {  // store unit placed after MFMA slot (0 .. 2 NM - 1), or -1
+    // The last step also loads, stores and reads "step nk" (zeros, inside the
+    // LDS array; never used).
+    auto pieces_at = [&](int s, int slot) __attribute__((always_inline)) {  // the pieces placed after MFMA slot (0 .. 2 NM - 1)
         const int d = slot - NM / 2;
-        return (d >= 0 && d % (NM / NU) == 0 && d / (NM / NU) < NU) ? d / (NM / NU) : -1;
+        if (d >= 0 && d < NM) store_pieces(s, (d * NPIECE) / NM, ((d + 1) * NPIECE) / NM);
     };
-    static_assert(NM % NU == 0 || NM / NU >= 1, "unit spacing");
     if (nk > 0) {
         load_step(0, ragged_k && nk == 1);
 #pragma unroll
@@ -433,32 +465,36 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, fa[0], fb[0], r);
+        load_step(1, false);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            load_step(kt + 1, ragged_k && kt + 2 == nk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
                 mfma_one(fa[0], fb[0], i);
                 __builtin_amdgcn_sched_barrier(0);
                 if (i < NR) read_one(cur, 1, fa[1], fb[1], i);
-                if (unit_at(i) >= 0) store_unit(cur ^ 1, unit_at(i));
+                if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1);
+                pieces_at(cur ^ 1, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int i = 0; i < NM / 2; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (unit_at(NM + i) >= 0) store_unit(cur ^ 1, unit_at(NM + i));
+                pieces_at(cur ^ 1, NM + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
+            const StepDesc nd = step_desc(kt + 2);
 #pragma unroll
             for (int i = NM / 2; i < NM; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
                 constexpr int H = NM - NM / 2;
                 const int j = i - NM / 2;
+#pragma unroll
+                for (int l = (j * NLOAD) / H; l < ((j + 1) * NLOAD) / H; ++l) load_one(nd, l);
 #pragma unroll
                 for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
                     read_one(cur ^ 1, 0, fa[0], fb[0], r);
