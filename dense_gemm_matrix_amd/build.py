@@ -18,6 +18,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels' main loops are fully unrolled schedules; let #pragma unroll
+    # expand the 3 x bf16 kernel's (larger than the default limit allows)
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-Wall",
 ]
 

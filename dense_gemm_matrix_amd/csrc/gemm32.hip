@@ -465,15 +465,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, fa[0], fb[0], r);
-        load_step(1, false);
+        {
+            const StepDesc d1 = step_desc(1);
+#pragma unroll
+            for (int l = 0; l < 2 * AR; ++l) load_one(d1, l);
+        }
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
+            const StepDesc nb = step_desc(kt + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
                 mfma_one(fa[0], fb[0], i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i < NR) read_one(cur, 1, fa[1], fb[1], i);
+                constexpr int Q = NM / 2;  // the slots before the first store piece
+                if (i < Q) {
+#pragma unroll
+                    for (int r = (i * NR) / Q; r < ((i + 1) * NR) / Q; ++r)
+                        read_one(cur, 1, fa[1], fb[1], r);
+#pragma unroll
+                    for (int l = (i * KB) / Q; l < ((i + 1) * KB) / Q; ++l) load_one(nb, 2 * AR + l);
+                }
                 if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1);
                 pieces_at(cur ^ 1, i);
                 __builtin_amdgcn_sched_barrier(0);
@@ -494,7 +506,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
                 constexpr int H = NM - NM / 2;
                 const int j = i - NM / 2;
 #pragma unroll
-                for (int l = (j * NLOAD) / H; l < ((j + 1) * NLOAD) / H; ++l) load_one(nd, l);
+                for (int l = (j * 2 * AR) / H; l < ((j + 1) * 2 * AR) / H; ++l) load_one(nd, l);
 #pragma unroll
                 for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
                     read_one(cur ^ 1, 0, fa[0], fb[0], r);
