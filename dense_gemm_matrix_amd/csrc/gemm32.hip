@@ -96,41 +96,50 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
 
     u32x4 ra[NA], rb[KB];
 
-    auto load_step = [&](int kt, bool tail) {
+    // Global loads of step kt: step_desc makes the two resources, load_one
+    // issues load j (0 .. NLOAD - 1, A's first) so that the main loop can
+    // spread them over matrix instructions, mask_a zeroes A's columns at or
+    // past K on the last step of a ragged K (they hold other data: row
+    // padding or the next row; the matching B rows are zero).
+    constexpr int NLOAD = NA + KB;
+    struct StepDesc {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto step_desc = [&](int kt) {  // steps at or past the end: empty ranges (zeros)
         const int k0 = kt * BK;
+        const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 4;
-        const int64_t abytes = ((int64_t)(rows_a - 1) * lda + (K - k0)) * 4;
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(abase, abytes);
-        const int rows_b = (K - k0) < BK ? (K - k0) : BK;
+        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 4 : 0;
+        const int rows_b = krem < BK ? krem : BK;
         const char* bbase = B + ((int64_t)k0 * ldb + n0) * 4;
-        const int64_t bbytes = ((int64_t)(rows_b - 1) * ldb + cols_b) * 4;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(bbase, bbytes);
+        const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
+        return StepDesc{make_rsrc(abase, abytes), make_rsrc(bbase, bbytes)};
+    };
+    auto load_one = [&](const StepDesc& d, int j) {
+        if (j < NA)
+            ra[j] = load16(d.a, voff_a[j]);
+        else
+            rb[j - NA] = load16(d.b, voff_b[j - NA]);
+    };
+    auto mask_a = [&](int kt) {
+        const int valid = K - kt * BK - ac * 4;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) ra[i] = load16(rsa, voff_a[i]);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) rb[i] = load16(rsb, voff_b[i]);
-        if (tail) {
-            // Columns of A at or past K hold other data (row padding or the next
-            // row); they must be exact zeros, since the matching B rows are.
-            const int valid = K - k0 - ac * 4;
-#pragma unroll
-            for (int i = 0; i < NA; ++i) ra[i] = mask_tail32(ra[i], valid);
-        }
+        for (int i = 0; i < NA; ++i) ra[i] = mask_tail32(ra[i], valid);
     };
 
-    auto store_step = [&](int s) {
+    // Registers -> LDS stage s, in NSTORE pieces: piece i < NA writes A chunk
+    // i; piece NA + 4 h + cc writes B column cc's chunk h (KB K-rows x 4
+    // columns become 4 columns x KB / 4 chunks of 4 K values).
+    constexpr int NSTORE = NA + KB;
+    auto store_one = [&](int s, int p) {
+        if (p < NA) {
+            lds[s][0][lds32_index(ar0 + 32 * p, ac)] = ra[p];
+        } else {
+            const int h = (p - NA) / 4, cc = (p - NA) % 4;
+            u32x4 v;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) lds[s][0][lds32_index(ar0 + 32 * i, ac)] = ra[i];
-        // KB K-rows x 4 columns -> 4 columns x KB / 4 chunks of 4 K values.
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-            for (int h = 0; h < KB / 4; ++h) {
-                u32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
-                lds[s][1][lds32_index(nb * 4 + cc, kb * (KB / 4) + h)] = v;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
+            lds[s][1][lds32_index(nb * 4 + cc, kb * (KB / 4) + h)] = v;
         }
     };
 
@@ -162,49 +171,74 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
             b[nj] = lds[s][1][lds32_index(wn * (TB / 2) + nj * 32 + li, ch)];
     };
 
-    auto mfma_frags = [&](const u32x4 (&a)[MI], const u32x4 (&b)[MI]) {
+    // The MI x MI x 4 matrix instructions of one chunk pair (k-quarter e
+    // outermost, so consecutive ones use different accumulators); after
+    // instruction i, `after(i)` issues whatever the schedule places there.
+    constexpr int NMP = MI * MI * 4;
+    auto mfma_frags = [&](const u32x4 (&a)[MI], const u32x4 (&b)[MI], auto&& after) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int nj = 0; nj < MI; ++nj)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int nj = 0; nj < MI; ++nj) {
                     acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         as_float(a[mi][e]), as_float(b[nj][e]), acc[mi][nj], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    after((e * MI + mi) * MI + nj);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
     };
+    auto nothing = [](int) {};
 
-    // Schedule of one K step (stage `cur` in LDS, stage cur ^ 1 being filled):
-    // global loads for step kt + 1 -> registers; pairs 0, 1, 2: read the next
-    // pair's fragments, then compute; registers -> LDS stage cur ^ 1; barrier;
-    // read pair 0 of stage cur ^ 1, then compute pair 3 (already in registers),
+    // Schedule of one K step (stage `cur` in LDS, stage cur ^ 1 being filled),
+    // in issue order: read pair 1; pair 0's matrix instructions, with the
+    // global loads of step kt + 1 spread among them; read pair 2; pair 1; read
+    // pair 3; pair 2, with the register -> LDS stores of step kt + 1 spread
+    // among them (stage cur ^ 1 was last read before the previous barrier);
+    // barrier; read pair 0 of stage cur ^ 1; pair 3 (already in registers),
     // which covers that read's latency.  sched_barrier keeps the compiler from
-    // sinking the fragment reads down to their uses.
+    // sinking the fragment reads down to their uses and from gathering the
+    // loads and stores into blocks, which would stall the matrix pipe.
     if (nk > 0) {
-        load_step(0, ragged_k && nk == 1);
-        store_step(0);
+        {
+            const StepDesc d0 = step_desc(0);
+#pragma unroll
+            for (int j = 0; j < NLOAD; ++j) load_one(d0, j);
+            if (ragged_k && nk == 1) mask_a(0);
+#pragma unroll
+            for (int p = 0; p < NSTORE; ++p) store_one(0, p);
+        }
         __syncthreads();
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             const bool more = kt + 1 < nk;
-            if (more) load_step(kt + 1, ragged_k && kt + 2 == nk);
+            const StepDesc nd = step_desc(kt + 1);
             read_frags(cur, 1, fa[1], fb[1]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[0], fb[0]);
+            mfma_frags(fa[0], fb[0], [&](int i) {
+#pragma unroll
+                for (int j = (i * NLOAD) / NMP; j < ((i + 1) * NLOAD) / NMP; ++j) load_one(nd, j);
+            });
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur, 2, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[1], fb[1]);
+            mfma_frags(fa[1], fb[1], nothing);
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur, 3, fa[1], fb[1]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[0], fb[0]);
+            if (ragged_k && kt + 2 == nk) mask_a(kt + 1);
             __builtin_amdgcn_sched_barrier(0);
-            if (more) store_step(cur ^ 1);
+            mfma_frags(fa[0], fb[0], [&](int i) {
+#pragma unroll
+                for (int p = (i * NSTORE) / NMP; p < ((i + 1) * NSTORE) / NMP; ++p) store_one(cur ^ 1, p);
+            });
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[1], fb[1]);
+            mfma_frags(fa[1], fb[1], nothing);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
