@@ -103,8 +103,8 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 // measured 1060 us against 1078-1099 us for 256 x 256.
 struct TileCand { int bm, bn; double eff, pair; };
 constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0}, {192, 256, 0.95, 0.0}, {128, 128, 0.6, 1.26}};
-constexpr TileCand TILES32[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.85, 1.67}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.6, 1.22}};
+constexpr TileCand TILES32[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.85, 1.5}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.5, 1.22}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
 double rounds_factor(const TileCand& t, int64_t wgs) {
