@@ -478,16 +478,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 
     // Schedule of step kt (stage cur holds it, stage cur ^ 1 receives step
     // kt + 1), in issue order; sched_barrier pins it:
-    //   pair 0's NM MFMAs, the first NR each followed by one read of pair 1
-    //   and the first NLOAD by one global load of step kt + 1;
+    //   pair 0's first NM / 2 MFMAs, carrying the NR reads of pair 1 and the
+    //   KB global loads of step kt + 1's B, spread evenly;
     //   from the middle of pair 0 to the middle of pair 1 (NM MFMA slots), the
-    //   NPIECE store pieces, spread evenly: at 256 x 256 one or two per slot,
-    //   six VALU instructions or two LDS writes, few enough to issue while
-    //   the matrix instruction before them runs;
+    //   NPIECE store pieces of step kt + 1 (A rows, then B columns), spread
+    //   evenly: at 256 x 256 at most one per slot, six VALU instructions or two
+    //   LDS writes, few enough to issue while the matrix instruction before
+    //   them runs;
     //   barrier (stage cur ^ 1 complete; every read of stage cur issued);
-    //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0.
-    // The last step also loads, stores and reads "step nk" (zeros, inside the
-    // LDS array; never used).
+    //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0 and
+    //   the 2 AR global loads of step kt + 2's A into the registers the store
+    //   pieces have just emptied.
+    // No slot carries more than two memory instructions.  The last steps also
+    // load, split and store steps nk and nk + 1 (empty ranges: zeros, inside
+    // the LDS array; never read).
     auto pieces_at = [&](int s, int slot) __attribute__((always_inline)) {  // the pieces placed after MFMA slot (0 .. 2 NM - 1)
         const int d = slot - NM / 2;
         if (d >= 0 && d < NM) store_pieces(s, (d * NPIECE) / NM, ((d + 1) * NPIECE) / NM);
