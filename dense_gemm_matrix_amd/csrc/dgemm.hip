@@ -99,11 +99,13 @@ constexpr double REDUCE_FIXED_US = 3.0;   // launch and tail of the reduction ke
 constexpr double HBM_BYTES_PER_US = 5.0e6;
 constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% faster
 
-// pair = 0: one workgroup per CU.  fp32 at 4096^3: 128 x 128 (two per CU)
-// measured 1060 us against 1078-1099 us for 256 x 256.
+// pair = 0: one workgroup per CU.  fp32 has the 128 x 128 tile only: in a
+// sweep of forced plans 256 x 256 was slower at every shape (4096^3: 1049 us
+// against 1002 us), and the cost model never chose it; eff stays relative to
+// a 256 x 256 workgroup so that step_us keeps one meaning.
 struct TileCand { int bm, bn; double eff, pair; };
 constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0}, {192, 256, 0.95, 0.0}, {128, 128, 0.6, 1.26}};
-constexpr TileCand TILES32[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.85, 1.5}};
+constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5}};
 constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.5, 1.22}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
@@ -116,7 +118,7 @@ double rounds_factor(const TileCand& t, int64_t wgs) {
 // Candidate macro-tiles of an input format's kernel.
 const TileCand* tiles_for(int in, int& n) {
     if (in == IN_BF16 || in == IN_F16) { n = 3; return TILES16; }
-    if (in == IN_F32) { n = 2; return TILES32; }
+    if (in == IN_F32) { n = 1; return TILES32; }
     n = 2;
     return TILES32X3;
 }

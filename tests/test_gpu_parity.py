@@ -139,6 +139,36 @@ def test_exact_integer_full_size_freivalds(path):
     assert np.array_equal(Cn[rows], C64)
 
 
+@pytest.mark.parametrize("path", ["f32", "f32x3", "bf16", "f16"])
+@pytest.mark.parametrize("K", [1, 33, 65, 100])
+def test_largest_tile_with_few_ragged_k_steps(path, K):
+    """4096 x 4096 selects each path's largest tile (256 x 256 for the 16-bit
+    and 3 x bf16 kernels, 128 x 128 for fp32); K = 1, 33, 65, 100 gives one to
+    four K steps with a ragged last one, so the tail handling of the first step
+    and of a later step both run, with NaN in A's row padding.  Integer inputs:
+    C is exact, checked everywhere by Freivalds' identity and bit for bit on
+    sampled rows against the oracle."""
+    M = N = 4096
+    largest = {"f32": 128, "f32x3": 256, "bf16": 256, "f16": 256}[path]
+    assert dg.dgemm_tile_map(M, N, path)["tile_rows"] == largest
+    print(f"case largest-tile {path} K={K}", flush=True)
+    dtype = store(path)
+    A, B = pair(M, N, K, "ints", dtype, seed=3200 + K)
+    C = run(path, "f32", A, B, a_extra=8, b_extra=8)
+    Cn = to64(C)
+    Aw, Bw = oracle.widen(dtype, A), oracle.widen(dtype, B)
+    rng = np.random.default_rng(3300 + K)
+    for _ in range(2):
+        x = rng.integers(-4, 5, N).astype(np.float64)
+        assert np.array_equal(Cn @ x, Aw @ (Bw @ x))
+        y = rng.integers(-4, 5, M).astype(np.float64)
+        assert np.array_equal(y @ Cn, (y @ Aw) @ Bw)
+    rows = sample_rows(M, rng)
+    C64, _ = oracle.gemm(dtype, A, B, rows=rows)
+    assert np.array_equal(Cn[rows], C64)
+    assert gap_untouched(C)
+
+
 @pytest.mark.parametrize("path", ["bf16", "f16"])
 def test_exact_integer_192_tile_freivalds(path):
     """4000 x 3000 x 4104 selects the 192 x 256 macro-tile: integer inputs,
