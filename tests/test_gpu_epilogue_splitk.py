@@ -171,6 +171,40 @@ def test_split_k_exact_integers_bitwise_and_repeatable(path, out, M, N, K):
     assert torch.equal(C1, C2)
 
 
+# Split plans on the larger tiles: the smallest shapes (found by scanning the
+# planner) whose plan splits K on a 256 x 256 or 192 x 256 macro-tile.
+BIG_TILE_SPLITS = [("f32x3", "f32", 512, 6144, 2048, 256), ("bf16", "f32", 512, 6144, 12288, 256),
+                   ("f16", "f16", 512, 6144, 12288, 256), ("bf16", "bf16", 768, 4096, 8192, 192),
+                   ("f16", "f32", 768, 4096, 8192, 192)]
+
+
+@pytest.mark.parametrize("path,out,M,N,K,tile", BIG_TILE_SPLITS)
+def test_split_k_on_the_larger_tiles(path, out, M, N, K, tile):
+    """Integer inputs (every partial sum exact in fp32): every element of C is
+    written, sampled rows equal the oracle's rounding bit for bit, and an fp32 C
+    satisfies Freivalds' identity exactly."""
+    p = split_plan(path, out, M, N, K)
+    assert p["tile_rows"] == tile, p
+    print(f"case bigtile-split {path}->{out} {M}x{N}x{K} plan {p}", flush=True)
+    dtype = store(path)
+    A, B = pair(M, N, K, "ints", dtype, seed=5600 + M + K)
+    C, ws = run_ex(path, out, A, B, ws_bytes=p["workspace_bytes"])
+    Cn = to64(C)
+    assert not np.isnan(Cn).any(), "unwritten elements"
+    rng = np.random.default_rng(5601 + K)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, M - 1],
+                                     rng.integers(0, M, 12)]))
+    C64, _ = oracle.gemm(dtype, A, B, rows=rows)
+    assert np.array_equal(Cn[rows], oracle.widen(out, oracle.round_to(out, C64)))
+    if out == "f32":
+        Aw, Bw = oracle.widen(dtype, A), oracle.widen(dtype, B)
+        x = rng.integers(-4, 5, N).astype(np.float64)
+        assert np.array_equal(Cn @ x, Aw @ (Bw @ x))
+        y = rng.integers(-4, 5, M).astype(np.float64)
+        assert np.array_equal(y @ Cn, (y @ Aw) @ Bw)
+    assert gap_untouched(C) and spare_untouched(ws, p["workspace_bytes"])
+
+
 def test_one_gpu_row_share_of_4096_cubed():
     """512 x 4096 x 4096 bf16 (one GPU's share of 4096^3 split by rows over 8):
     the split plan through matmul, sampled rows against the oracle, and every
