@@ -155,6 +155,35 @@ def cpu_baseline(A, B, meta, target_s: float = 12.0):
                       f"{t:.1f} s"}
 
 
+def cpu_single_thread(meta_rows: int = 96):
+    """The oracle on one thread: the fp32 512^3 workload in full, and the first
+    meta_rows rows of the bf16 4096^3 product, extrapolated to all 4096 rows
+    (labelled as such) from a second run of meta_rows / 3 rows, which separates
+    the fixed cost (widening B) from the cost per row."""
+    import numpy as np
+    import oracle
+    from synth_inputs import workload
+    out = {"cores": 1, "kind": "oracle"}
+    A, B, m = workload("f32_512")
+    t0 = time.perf_counter()
+    oracle.gemm(m["dtype"], A, B, nthreads=1)
+    t = time.perf_counter() - t0
+    out["f32_512_full"] = {"s": round(t, 3), "tflops": round(tflops(m["M"], m["N"], m["K"], t), 6)}
+    A, B, m = workload("bf16_4096")
+    ts = []
+    for r in (meta_rows // 3, meta_rows):
+        t0 = time.perf_counter()
+        oracle.gemm(m["dtype"], A, B, rows=np.arange(r), nthreads=1)
+        ts.append(time.perf_counter() - t0)
+    per_row = max((ts[1] - ts[0]) / (meta_rows - meta_rows // 3), 1e-9)
+    fixed = max(ts[0] - per_row * (meta_rows // 3), 0.0)
+    out["bf16_4096_rows"] = {"rows": meta_rows, "s": round(ts[1], 3),
+                             "fixed_s": round(fixed, 3), "per_row_s": round(per_row, 5),
+                             "extrapolated_full_s": round(fixed + per_row * m["M"], 1),
+                             "tflops": round(tflops(meta_rows, m["N"], m["K"], ts[1]), 6)}
+    return out
+
+
 def _smi_values(node, key):
     """All numeric 'value' fields under dict keys starting with `key`."""
     out = []
@@ -450,6 +479,7 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)
+        line["cpu_single_thread"] = cpu_single_thread()
     print(json.dumps(line), flush=True)
 
 
