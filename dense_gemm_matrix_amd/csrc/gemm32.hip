@@ -479,18 +479,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 
     // Schedule of step kt (stage cur holds it, stage cur ^ 1 receives step
     // kt + 1), in issue order; sched_barrier pins it:
-    //   pair 0's first NM / 2 MFMAs, carrying the NR reads of pair 1 and the
-    //   KB global loads of step kt + 1's B, spread evenly;
+    //   pair 0's first NM / 2 MFMAs, carrying the NR reads of pair 1;
     //   from the middle of pair 0 to the middle of pair 1 (NM MFMA slots), the
     //   NPIECE store pieces of step kt + 1 (A rows, then B columns), spread
     //   evenly: at 256 x 256 at most one per slot, six VALU instructions or two
     //   LDS writes, few enough to issue while the matrix instruction before
-    //   them runs;
+    //   them runs; pair 1's first half also carries the 2 AR global loads of
+    //   step kt + 2's A (the A pieces have emptied those registers);
     //   barrier (stage cur ^ 1 complete; every read of stage cur issued);
     //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0 and
-    //   the 2 AR global loads of step kt + 2's A into the registers the store
-    //   pieces have just emptied.
-    // No slot carries more than two memory instructions.  The last steps also
+    //   the KB loads of step kt + 2's B (the B pieces have emptied those).
+    // Every load is thus issued about NM slots before its first use, and no
+    // slot carries more than two memory instructions.  The last steps also
     // load, split and store steps nk and nk + 1 (empty ranges: zeros, inside
     // the LDS array; never read).
     auto pieces_at = [&](int s, int slot) __attribute__((always_inline)) {  // the pieces placed after MFMA slot (0 .. 2 NM - 1)
@@ -504,14 +504,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, fa[0], fb[0], r);
-        {
-            const StepDesc d1 = step_desc(1);
-#pragma unroll
-            for (int l = 0; l < 2 * AR; ++l) load_one(d1, l);
-        }
+        load_step(1, false);  // step 1's tail mask, if any, is applied in the loop
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            const StepDesc nb = step_desc(kt + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
@@ -522,30 +517,32 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 #pragma unroll
                     for (int r = (i * NR) / Q; r < ((i + 1) * NR) / Q; ++r)
                         read_one(cur, 1, fa[1], fb[1], r);
-#pragma unroll
-                    for (int l = (i * KB) / Q; l < ((i + 1) * KB) / Q; ++l) load_one(nb, 2 * AR + l);
                 }
                 if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1);
                 pieces_at(cur ^ 1, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // Step kt + 2's loads: A's into the registers the A pieces have just
+            // emptied, B's after the barrier, each about 48 slots before use.
+            const StepDesc nd = step_desc(kt + 2);
+            constexpr int H = NM - NM / 2;
 #pragma unroll
             for (int i = 0; i < NM / 2; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int l = (i * 2 * AR) / H; l < ((i + 1) * 2 * AR) / H; ++l) load_one(nd, l);
                 pieces_at(cur ^ 1, NM + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
-            const StepDesc nd = step_desc(kt + 2);
 #pragma unroll
             for (int i = NM / 2; i < NM; ++i) {
                 mfma_one(fa[1], fb[1], i);
                 __builtin_amdgcn_sched_barrier(0);
-                constexpr int H = NM - NM / 2;
                 const int j = i - NM / 2;
 #pragma unroll
-                for (int l = (j * 2 * AR) / H; l < ((j + 1) * 2 * AR) / H; ++l) load_one(nd, l);
+                for (int l = (j * KB) / H; l < ((j + 1) * KB) / H; ++l) load_one(nd, 2 * AR + l);
 #pragma unroll
                 for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
                     read_one(cur ^ 1, 0, fa[0], fb[0], r);
