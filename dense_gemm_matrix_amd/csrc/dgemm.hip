@@ -85,14 +85,15 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // rounds = ceil(tiles * s / 256) workgroups per CU.  128 x 128 tiles fit two
 // workgroups on a CU: two co-resident ones take `pair` times as long as one
 // alone (measured: bf16 1.26, fp32 1.67), so for them rounds counts pairs and
-// the term in parentheses is multiplied by `pair`.
+// the term in parentheses is multiplied by `pair`.  A grid of at most one
+// workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
+// runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU.
 // A grid of fewer tiles than CUs, or K much deeper than M and N, is where
 // splitting pays (the nine-levels tutorial's section 2.9 names Split-K for
 // small-matrix parallelism); everywhere else the unsplit plan wins.  The
 // constants were checked against a sweep of forced plans over 18 shapes: the
 // plan chosen is within 8 % of the fastest measured one on every shape.
 
-constexpr int NUM_CU = 256;
 constexpr int MAX_SPLITS = 16;
 constexpr double WG_FIXED_US = 1.0;       // prologue + epilogue per round of workgroups
 constexpr double REDUCE_FIXED_US = 3.0;   // launch and tail of the reduction kernel
@@ -103,10 +104,11 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 // sweep of forced plans 256 x 256 was slower at every shape (4096^3: 1049 us
 // against 1002 us), and the cost model never chose it; eff stays relative to
 // a 256 x 256 workgroup so that step_us keeps one meaning.
-struct TileCand { int bm, bn; double eff, pair; };
-constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0}, {192, 256, 0.95, 0.0}, {128, 128, 0.6, 1.26}};
-constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0}, {128, 128, 0.5, 1.22}};
+struct TileCand { int bm, bn; double eff, pair, eff1; };
+constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 1.0}, {192, 256, 0.95, 0.0, 0.95},
+                                {128, 128, 0.6, 1.26, 0.8}};
+constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 0.85}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0}, {128, 128, 0.5, 1.22, 0.5}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
 double rounds_factor(const TileCand& t, int64_t wgs) {
@@ -114,6 +116,9 @@ double rounds_factor(const TileCand& t, int64_t wgs) {
     if (t.pair > 0.0 && per_cu >= 2) return (double)((per_cu + 1) / 2) * t.pair;
     return (double)per_cu;
 }
+
+// Throughput of tile t relative to a 256 x 256 workgroup in a grid of `wgs`.
+double tile_eff(const TileCand& t, int64_t wgs) { return wgs <= NUM_CU ? t.eff1 : t.eff; }
 
 // Candidate macro-tiles of an input format's kernel.
 const TileCand* tiles_for(int in, int& n) {
@@ -153,7 +158,7 @@ TileCand pick_tile(int in, int M, int N) {
     for (int i = 0; i < n; ++i) {
         const TileCand& c = cands[i];
         const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-        const double cost = rounds_factor(c, tiles) * c.bm * c.bn / c.eff;
+        const double cost = rounds_factor(c, tiles) * c.bm * c.bn / tile_eff(c, tiles);
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c; }
     }
     return best;
@@ -162,8 +167,10 @@ TileCand pick_tile(int in, int M, int N) {
 double estimate_us(int in, int es_out, int M, int N, const TileCand& t, int splits,
                    int steps_per_split, int ldw) {
     const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
-    double us = rounds_factor(t, tiles * splits) *
-                (steps_per_split * step_us(in) * t.bm * t.bn / 65536.0 / t.eff + WG_FIXED_US);
+    const int64_t wgs = tiles * splits;
+    double us = rounds_factor(t, wgs) *
+                (steps_per_split * step_us(in) * t.bm * t.bn / 65536.0 / tile_eff(t, wgs) +
+                 WG_FIXED_US);
     if (splits > 1)
         us += REDUCE_FIXED_US + (2.0 * splits * M * (double)ldw * 4 + (double)M * N * es_out) /
                                     HBM_BYTES_PER_US;
@@ -226,6 +233,12 @@ int run(int in, int outfmt, int M, int N, int K, const void* A, int lda, const v
     L.tiles_n = (int)ceil_div(N, p.bn);
     if ((int64_t)L.tiles_m * L.tiles_n > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
     L.stream = stream;
+    // The 16-bit 128 x 128 tile: two workgroups share a CU with a 2-stage ring
+    // (64 KiB of LDS each); when the grid has no more workgroups than CUs there is
+    // no second one to hide load latency, and a 4-stage ring (128 KiB, loads
+    // issued three steps ahead) measured 17-27 % faster.
+    const int64_t wgs = (int64_t)L.tiles_m * L.tiles_n * p.splits;
+    L.stages = (p.bm == 128 && (in == IN_BF16 || in == IN_F16) && wgs <= NUM_CU) ? 4 : 2;
     if (p.splits == 1) {
         L.out = outfmt;
         L.epi = epi_needed(e);

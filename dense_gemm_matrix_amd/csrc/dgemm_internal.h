@@ -15,6 +15,7 @@ enum OutFmt { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 constexpr int NTHREADS = 256;   // 4 waves: the fp32 kernels' workgroup
 constexpr int GROUP_M = 4;      // tile rows per strip in the tile walk
 constexpr int NUM_XCD = 8;      // XCDs that workgroups are dealt across
+constexpr int NUM_CU = 256;     // compute units of an MI355X
 
 inline int in_esize(int in) { return (in == IN_F32 || in == IN_F32X3) ? 4 : 2; }
 inline int out_esize(int out) { return out == OUT_F32 ? 4 : 2; }
@@ -56,7 +57,8 @@ struct EpiArgs {
 // splits = 1 and kchunk = K.
 struct GemmLaunch {
     int in, out, tbm, tbn;
-    bool epi;  // apply `e` in the kernel (only with splits == 1)
+    int stages;  // LDS stages of the 16-bit kernel's ring (2, or 4 at 128 x 128)
+    bool epi;    // apply `e` in the kernel (only with splits == 1)
     const char* A;
     const char* B;
     char* C;

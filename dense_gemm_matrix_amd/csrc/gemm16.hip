@@ -1,10 +1,13 @@
 // gemm16.hip -- the bf16 / fp16 GEMM kernel for gfx950 (MI355X).
 //
 // Both operands go global -> LDS with direct-to-LDS buffer loads (no VGPR
-// staging, no LDS write instructions) into a ring of S16 stages of BK16-deep
-// slabs (2 x 64 at present: of the settings that fit 160 KiB, measured
-// fastest; 4 x 32 and 5 x 32 were slower), each issued one step before its
-// use.  A is stored K-contiguous and read with ds_read_b128.  B is stored as it
+// staging, no LDS write instructions) into a ring of S stages of BK16 = 64-deep
+// slabs, each issued S - 1 steps before its use.  S = 2 for the 256-wide tiles
+// (of the settings that fit 160 KiB, measured fastest; 4 x 32 and 5 x 32 deep
+// were slower).  The 128 x 128 tile has both S = 2 (64 KiB: two workgroups per
+// CU, each hiding the other's load latency) and S = 4 (128 KiB: one workgroup
+// per CU, loads issued three steps ahead); the planner takes S = 4 when the
+// grid has no more workgroups than CUs.  A is stored K-contiguous and read with ds_read_b128.  B is stored as it
 // lies in memory (row-major, N-contiguous) and read with ds_read_b64_tr_b16:
 // within each 16-lane group that instruction performs a 4 x 4 transpose of
 // 4-element row pieces, which hands every lane the four consecutive k of one
@@ -37,7 +40,6 @@ namespace dgemm {
 namespace {
 
 constexpr int BK16 = 64;                       // K per stage
-constexpr int S16 = 2;                         // LDS stages
 constexpr int KP16 = BK16 / 16;                // 16-k chunk pairs per stage
 constexpr int A16_CH = BK16 / 8;               // 16-byte chunks per A row
 constexpr int A16_ROW = BK16 * 2;              // bytes per staged A row
@@ -45,9 +47,10 @@ constexpr int A16_RPB = 1024 / A16_ROW;        // A rows per 1 KiB load block
 
 // Macro-tile TBM x TBN, 2 x WN waves (WN = 2: 4 waves, one per SIMD; WN = 4:
 // 8 waves, two per SIMD), each wave (TBM/2) x (TBN/WN) = MI x NJ blocks of
-// 32 x 32 accumulators.
-template <int TBM, int TBN, int WN = 2>
+// 32 x 32 accumulators, and an LDS ring of S stages.
+template <int TBM, int TBN, int WN = 2, int S_ = 2>
 struct Tile16 {
+    static constexpr int S = S_;                         // LDS stages
     static constexpr int NW = 2 * WN;                    // waves
     static constexpr int NT = 64 * NW;                   // threads
     static constexpr int MI = TBM / 64;
@@ -65,8 +68,8 @@ struct Tile16 {
     static_assert(TBM % 64 == 0 && TBN % (32 * WN) == 0 && TBM <= NT, "tile shape");
     static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0,
                   "whole load blocks per wave");
-    static_assert(S16 * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
-    static_assert((S16 - 1) * LOADS <= 63, "vmcnt range");
+    static_assert(S * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
+    static_assert(S >= 2 && (S - 1) * LOADS <= 63, "stages, vmcnt range");
 };
 
 // Byte offset of chunk c (0..7) of A row r in a stage.  ds_read_b128 serves
@@ -86,12 +89,12 @@ __device__ __forceinline__ int b16_off(int k, int chunk, int row_bytes) {
     return k * row_bytes + ((chunk ^ b16_swz(k)) << 4);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN>
-__global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
+template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN, int S>
+__global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
     int kchunk, int64_t c_zstride, EpiArgs epi) {
-    using T = Tile16<TBM, TBN, WN>;
+    using T = Tile16<TBM, TBN, WN, S>;
     // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
     // and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when unsplit).
     {
@@ -103,9 +106,9 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
         K = (K - kbeg) < kchunk ? (K - kbeg) : kchunk;
     }
     constexpr int MI = T::MI, NJ = T::NJ;
-    __shared__ __attribute__((aligned(1024))) char smem[S16 * (T::A_STAGE + T::B_STAGE)];
+    __shared__ __attribute__((aligned(1024))) char smem[T::S * (T::A_STAGE + T::B_STAGE)];
     char* const smA = smem;
-    char* const smB = smem + S16 * T::A_STAGE;
+    char* const smB = smem + T::S * T::A_STAGE;
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -137,14 +140,14 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
         voffB[j] = kB * ldb * 2 + cB * 16;
     }
 
-    // Global loads of step kt into LDS stage kt % S16, one instruction at a
+    // Global loads of step kt into LDS stage kt % S, one instruction at a
     // time: stage_desc computes the step's two descriptors, dma_one(j) issues
     // load j (A loads first, then B).  Steps past the end get empty ranges
     // (they only keep the per-step load count uniform).
     struct StageDesc { __amdgpu_buffer_rsrc_t ra, rb; int s; };
     auto stage_desc = [&](int kt) {
         StageDesc d;
-        d.s = kt % S16;
+        d.s = kt % T::S;
         const int k0 = kt * BK16;
         const int krem = K - k0;
         const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
@@ -176,7 +179,7 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
     // rows past K are already zero (outside the descriptor's range).
     auto fix_tail = [&]() {
         const int kt = nk - 1;
-        const int s = kt % S16;
+        const int s = kt % T::S;
         const int kin = K - kt * BK16;       // valid k in the last stage, 1..BK16-1
         const int chunk0 = kin >> 3;         // first chunk holding an invalid element
         char* rowp = smA + s * T::A_STAGE;
@@ -217,10 +220,10 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
     // reads, then 2 NJ B transpose reads (nj = (i - MI) / 2, half (i - MI) % 2).
     auto read_piece = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2], int i) {
         if (i < MI) {
-            const char* sa = smA + (kt % S16) * T::A_STAGE;
+            const char* sa = smA + (kt % T::S) * T::A_STAGE;
             a[i] = *(const u32x4*)(sa + a16_off(wm * (TBM / 2) + i * 32 + li, 2 * kp + g));
         } else {
-            const char* sb = smB + (kt % S16) * T::B_STAGE;
+            const char* sb = smB + (kt % T::S) * T::B_STAGE;
             const int nj = (i - MI) >> 1, h = (i - MI) & 1;
             const int k = kp * 16 + 8 * g + 4 * h + ta;
             const int c = wn * (TBN / WN / 8) + nj * 4 + 2 * tg + (tq >> 1);
@@ -252,19 +255,19 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    using OneStepLeft = std::integral_constant<int, (S16 - 1) * T::LOADS>;
-    using TwoStepsLeft = std::integral_constant<int, (S16 - 2) * T::LOADS>;
+    using OneStepLeft = std::integral_constant<int, (T::S - 1) * T::LOADS>;
+    using TwoStepsLeft = std::integral_constant<int, (T::S - 2) * T::LOADS>;
 
-    // Schedule (S16 stages, KP16 chunk pairs per step), written out in issue
+    // Schedule (S stages, KP16 chunk pairs per step), written out in issue
     // order: with one wave per SIMD nothing else hides a stall, so every
     // load and LDS read sits between two MFMAs (sched_barrier pins the order).
-    // Prologue: loads of steps 0 .. S16 - 1.  Step kt: spread over the MFMAs
+    // Prologue: loads of steps 0 .. S - 1.  Step kt: spread over the MFMAs
     // of pairs 0 and 1, read the fragments of pairs 1 .. KP16 - 1 (one
     // register set per pair; each pair's reads are issued before its MFMAs
     // start); then wait until step kt + 1 has landed (later steps may still be
     // in flight) and barrier, which retires every wave's reads of stage
-    // kt % S16; then, spread over the MFMAs of pairs 2 .. KP16 - 1, refill that
-    // stage with step kt + S16, and during the last pair read pair 0 of step
+    // kt % S; then, spread over the MFMAs of pairs 2 .. KP16 - 1, refill that
+    // stage with step kt + S, and during the last pair read pair 0 of step
     // kt + 1.  (A barrier after pair 0, with the refill over three pairs,
     // measured about 1 % slower.)
     // The last step reads that pair too (from the stage the empty loads past
@@ -272,7 +275,7 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
     // used): an unconditional read saves a branch per matrix instruction.
     if (nk > 0) {
 #pragma unroll
-        for (int s = 0; s < S16; ++s) issue_stage(s);
+        for (int s = 0; s < T::S; ++s) issue_stage(s);
         sync(OneStepLeft{});
         if ((K % BK16) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
         read_frags(0, 0, fa[0], fb[0]);
@@ -290,8 +293,8 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
             // Every read of stage kt is now issued: retire them, wait for step
-            // kt + 1, barrier.  The stage is then free for step kt + S16.
-            const StageDesc d = stage_desc(kt + S16);
+            // kt + 1, barrier.  The stage is then free for step kt + S.
+            const StageDesc d = stage_desc(kt + T::S);
             sync(TwoStepsLeft{});
             if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
             constexpr int SLOTS = T::NMFMA * (KP16 - 2);
@@ -323,7 +326,7 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN>::NT)) void gemm16_kernel(
                                  epi, m0 + TBM <= M && n0 + TBN <= N);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN = 2>
+template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN = 2, int S = 2>
 hipError_t go(const GemmLaunch& L) {
     const char* a = L.A;
     const char* b = L.B;
@@ -333,9 +336,9 @@ hipError_t go(const GemmLaunch& L) {
     int64_t zs = L.c_zstride;
     EpiArgs e = L.e;
     void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &kchunk, &zs, &e};
-    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI, WN>,
+    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI, WN, S>,
                            dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits),
-                           dim3(Tile16<TBM, TBN, WN>::NT),
+                           dim3(Tile16<TBM, TBN, WN, S>::NT),
                            args, 0, L.stream);
 }
 
@@ -343,7 +346,8 @@ template <int IN, int OUT, bool EPI>
 hipError_t by_tile(const GemmLaunch& L) {
     if (L.tbm == 256 && L.tbn == 256) return go<IN, OUT, 256, 256, EPI>(L);
     if (L.tbm == 192 && L.tbn == 256) return go<IN, OUT, 192, 256, EPI>(L);
-    if (L.tbm == 128 && L.tbn == 128) return go<IN, OUT, 128, 128, EPI>(L);
+    if (L.tbm == 128 && L.tbn == 128)
+        return L.stages == 4 ? go<IN, OUT, 128, 128, EPI, 2, 4>(L) : go<IN, OUT, 128, 128, EPI, 2, 2>(L);
     return hipErrorInvalidValue;
 }
 

@@ -170,6 +170,39 @@ def test_largest_tile_with_few_ragged_k_steps(path, K):
 
 
 @pytest.mark.parametrize("path", ["bf16", "f16"])
+@pytest.mark.parametrize("M,N,K", [
+    (2048, 4096, 1), (2048, 4096, 130), (2000, 4000, 4104),               # > 256 workgroups
+    (1000, 2000, 1), (1000, 2000, 65), (1000, 2000, 200), (2048, 2048, 4104),  # <= 256
+])
+def test_128_tile_with_either_ring_depth(path, M, N, K):
+    """The 16-bit 128 x 128 tile keeps a 2-stage LDS ring when the grid has more
+    workgroups than the chip's 256 CUs and a 4-stage one otherwise.  K = 1, 65,
+    130 and 200 give fewer K steps than the deeper ring has stages, or exactly as
+    many, with a ragged last step; 4104 gives 65 steps with a ragged one.
+    Integer inputs, fp32 C: exact, checked everywhere by Freivalds' identity and
+    bit for bit on sampled rows against the oracle."""
+    tm = dg.dgemm_tile_map(M, N, path)
+    assert tm["tile_rows"] == 128 and tm["tile_cols"] == 128
+    ring = 4 if tm["num_wg"] <= 256 else 2
+    assert ring == (4 if M * N <= 2048 * 2048 else 2)
+    print(f"case tile128 {path} {M}x{N}x{K} ring {ring}", flush=True)
+    A, B = pair(M, N, K, "ints", path, seed=3400 + K + M)
+    C = run(path, "f32", A, B, a_extra=8, b_extra=8)
+    Cn = to64(C)
+    Aw, Bw = oracle.widen(path, A), oracle.widen(path, B)
+    rng = np.random.default_rng(3500 + K + M)
+    for _ in range(2):
+        x = rng.integers(-4, 5, N).astype(np.float64)
+        assert np.array_equal(Cn @ x, Aw @ (Bw @ x))
+        y = rng.integers(-4, 5, M).astype(np.float64)
+        assert np.array_equal(y @ Cn, (y @ Aw) @ Bw)
+    rows = sample_rows(M, rng)
+    C64, _ = oracle.gemm(path, A, B, rows=rows)
+    assert np.array_equal(Cn[rows], C64)
+    assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("path", ["bf16", "f16"])
 def test_exact_integer_192_tile_freivalds(path):
     """4000 x 3000 x 4104 selects the 192 x 256 macro-tile: integer inputs,
     fp32 C, checked everywhere by Freivalds' identity and on sampled rows
