@@ -258,3 +258,25 @@ def test_plan_invariants(M, N, K, fmt, ws):
         steps = -(-nk // p["splits"])
         # every split gets at least one K step, and the splits cover K exactly once
         assert (p["splits"] - 1) * steps < nk <= p["splits"] * steps
+
+
+def test_header_is_plain_c_and_the_c_client_links():
+    """include/dgemm.h compiles as C11 (-Wall -Wextra -Werror) in the C test
+    client, and the client built by build() resolves libdgemm.so in-tree."""
+    import shutil
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    src = os.path.join(here, "c_client", "gemm_client.c")
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    subprocess.run([gcc, "-std=c11", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include", src],
+                   check=True)
+    binary = os.path.join(here, "c_client", "gemm_client")
+    assert os.path.exists(binary), "run build() first"
+    ldd = subprocess.run(["ldd", binary], capture_output=True, text=True, check=True).stdout
+    line = [l for l in ldd.splitlines() if "libdgemm.so" in l]
+    assert line and os.path.join(root, "dense_gemm_matrix_amd") in os.path.realpath(
+        line[0].split("=>")[1].split("(")[0].strip()), ldd
