@@ -241,6 +241,12 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
                 __builtin_bit_cast(f16x8, a[mi]), __builtin_bit_cast(f16x8, bv), acc[mi][nj], 0, 0, 0);
         }
     };
+    // Block column of MFMA i of a chunk pair: rows in turn, odd rows right to
+    // left, so consecutive MFMAs always share one operand register set (the
+    // row-major order changes both at each new row).  Fewer operand bits change
+    // per instruction; at the board's power limit that measured ~0.5 % faster.
+    // Each accumulator still sees its k in the same order: the same results.
+    auto snake = [](int i) { return ((i / NJ) & 1) ? NJ - 1 - i % NJ : i % NJ; };
     auto read_frags = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2]) {
 #pragma unroll
         for (int i = 0; i < T::NREAD; ++i) read_piece(kt, kp, a, b, i);
@@ -283,8 +289,8 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
             constexpr int NR = T::NREAD * (KP16 - 1);
 #pragma unroll
             for (int i = 0; i < 2 * T::NMFMA; ++i) {
-                if (i < T::NMFMA) mfma_one(fa[0], fb[0], i / NJ, i % NJ);
-                else mfma_one(fa[1], fb[1], (i - T::NMFMA) / NJ, (i - T::NMFMA) % NJ);
+                if (i < T::NMFMA) mfma_one(fa[0], fb[0], i / NJ, snake(i));
+                else mfma_one(fa[1], fb[1], (i - T::NMFMA) / NJ, snake(i - T::NMFMA));
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = (i * NR) / (2 * T::NMFMA); r < ((i + 1) * NR) / (2 * T::NMFMA); ++r)
@@ -302,7 +308,7 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
             for (int kp = 2; kp < KP16; ++kp) {
 #pragma unroll
                 for (int i = 0; i < T::NMFMA; ++i) {
-                    mfma_one(fa[kp], fb[kp], i / NJ, i % NJ);
+                    mfma_one(fa[kp], fb[kp], i / NJ, snake(i));
                     __builtin_amdgcn_sched_barrier(0);
                     const int slot = (kp - 2) * T::NMFMA + i;
 #pragma unroll
