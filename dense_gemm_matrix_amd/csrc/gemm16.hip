@@ -273,9 +273,11 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
     // start); then wait until step kt + 1 has landed (later steps may still be
     // in flight) and barrier, which retires every wave's reads of stage
     // kt % S; then, spread over the MFMAs of pairs 2 .. KP16 - 1, refill that
-    // stage with step kt + S, and during the last pair read pair 0 of step
-    // kt + 1.  (A barrier after pair 0, with the refill over three pairs,
-    // measured about 1 % slower.)
+    // stage with step kt + S and read pair 0 of step kt + 1 (its stage landed
+    // before the barrier, and pair 0's registers are free).  Spreading those
+    // reads over both pairs rather than the last one measured 1-4 % faster on
+    // the tiles that are not power-limited.  (A barrier after pair 0, with the
+    // refill over three pairs, measured about 1 % slower.)
     // The last step reads that pair too (from the stage the empty loads past
     // K have zero-filled, inside the LDS array; the registers are never
     // used): an unconditional read saves a branch per matrix instruction.
@@ -315,11 +317,9 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
                     for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
                         dma_one(d, j);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (kp == KP16 - 1) {
 #pragma unroll
-                        for (int r = (i * T::NREAD) / T::NMFMA; r < ((i + 1) * T::NREAD) / T::NMFMA; ++r)
-                            read_piece(kt + 1, 0, fa[0], fb[0], r);
-                    }
+                    for (int r = (slot * T::NREAD) / SLOTS; r < ((slot + 1) * T::NREAD) / SLOTS; ++r)
+                        read_piece(kt + 1, 0, fa[0], fb[0], r);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
