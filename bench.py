@@ -7,8 +7,9 @@ that one kernel) on inputs already resident in HBM.  The headline line is the
 bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
 fp32-input 4096^3 products are measured the same way and reported under
 "per_dtype".  Also reported: the same product from a cold cache (each launch
-after a 512 MiB write), and the graphics clock and socket power amd-smi reads
-while the product runs.  The other parity workloads, and one GPU's row share of the 4096^3
+after a 512 MiB write), torch.matmul (hipBLASLt) on the same inputs for context,
+and the graphics clock and socket power amd-smi reads while the product runs.  The
+other parity workloads, and one GPU's row share of the 4096^3
 product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
 the planner splits K, through gemm_ex with a workspace; each both launched call by
 call from Python and replayed from a HIP graph (the small shapes are otherwise
@@ -16,7 +17,7 @@ bound by the host's launch rate).
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
-                    [--no-power-clock] [--no-cold-cache]
+                    [--no-power-clock] [--no-cold-cache] [--no-vendor]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -109,6 +110,27 @@ def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(stop) * 1e-3 / steps, wall
+
+
+def vendor_library(Ad, Bd, steps: int, warmup: int):
+    """torch.matmul on the same device inputs (hipBLASLt on ROCm), timed like
+    time_gemm, for context only.  Its C has the input format (for 16-bit inputs
+    torch's product writes a 16-bit C), so its epilogue writes half the bytes of
+    an fp32 C."""
+    import torch
+    Cv = torch.empty((Ad.shape[0], Bd.shape[1]), dtype=Ad.dtype, device=Ad.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        torch.matmul(Ad, Bd, out=Cv)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        torch.matmul(Ad, Bd, out=Cv)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e-3 / steps
 
 
 def cpu_baseline(A, B, meta, target_s: float = 12.0):
@@ -396,6 +418,7 @@ def main():
     ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--no-power-clock", action="store_true")
     ap.add_argument("--no-cold-cache", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the torch.matmul comparison")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -452,6 +475,13 @@ def main():
         t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
         line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
                               "launches": 20, "how": "each launch after writing a 512 MiB buffer"}
+    if not args.no_vendor:
+        print("bench: timing torch.matmul on the same inputs", file=sys.stderr, flush=True)
+        t_v = vendor_library(Ad, Bd, args.steps, min(args.warmup, 50))
+        line["vendor_library"] = {
+            "what": f"torch.matmul (hipBLASLt) on the same device inputs, C in {args.dtype}",
+            "us": round(t_v * 1e6, 2), "tflops": round(tflops(M, N, K, t_v), 2),
+            "frac_of_peak": round(tflops(M, N, K, t_v) / peak, 4)}
     if not args.no_power_clock:
         print("bench: sampling clock and power under load", file=sys.stderr, flush=True)
         line["power_clock"] = power_clock(entry[args.dtype], Ad, Bd, Cd, per_launch, value, peak)
