@@ -84,15 +84,19 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // reduce_bytes counts the partial sums written and read back plus C, and
 // rounds = ceil(tiles * s / 256) workgroups per CU.  128 x 128 tiles fit two
 // workgroups on a CU: two co-resident ones take `pair` times as long as one
-// alone (measured: bf16 1.26, fp32 1.67), so for them rounds counts pairs and
+// alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them rounds counts pairs and
 // the term in parentheses is multiplied by `pair`.  A grid of at most one
 // workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
 // runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU.
 // A grid of fewer tiles than CUs, or K much deeper than M and N, is where
 // splitting pays (the nine-levels tutorial's section 2.9 names Split-K for
 // small-matrix parallelism); everywhere else the unsplit plan wins.  The
-// constants were checked against a sweep of forced plans over 18 shapes: the
-// plan chosen is within 8 % of the fastest measured one on every shape.
+// constants were fitted to sweeps of forced plans (every candidate tile, split
+// counts 1 to 16, each timed twice).  The latest, 23 bf16 shapes from 512^3 to
+// 16384 x 4096 x 4096: the chosen plan is the fastest one timed on 20 of the 22
+// shapes whose plan was among those timed and within 2.4 % on the other two;
+// fp32 and 3 x bf16 (9 shapes each): the fastest on all fp32 shapes, within
+// 12.2 % on the 3 x bf16 ones.
 
 constexpr int MAX_SPLITS = 16;
 constexpr double WG_FIXED_US = 1.0;       // prologue + epilogue per round of workgroups
