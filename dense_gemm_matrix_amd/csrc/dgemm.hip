@@ -87,7 +87,9 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them rounds counts pairs and
 // the term in parentheses is multiplied by `pair`.  A grid of at most one
 // workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
-// runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU.
+// runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU,
+// and the 3 x bf16 one is measured faster alone on its CU than its pair factor
+// implies.
 // A grid of fewer tiles than CUs, or K much deeper than M and N, is where
 // splitting pays (the nine-levels tutorial's section 2.9 names Split-K for
 // small-matrix parallelism); everywhere else the unsplit plan wins.  The
@@ -95,8 +97,8 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // counts 1 to 16, each timed twice).  The latest, 23 bf16 shapes from 512^3 to
 // 16384 x 4096 x 4096: the chosen plan is the fastest one timed on 20 of the 22
 // shapes whose plan was among those timed and within 2.4 % on the other two;
-// fp32 and 3 x bf16 (9 shapes each): the fastest on all fp32 shapes, within
-// 12.2 % on the 3 x bf16 ones.
+// fp32 (9 shapes): the fastest on all; 3 x bf16 (12 shapes, after the 128 x 128
+// tile's two staging sets): the fastest on 10, within 7.2 % on all.
 
 constexpr int MAX_SPLITS = 16;
 constexpr double WG_FIXED_US = 1.0;       // prologue + epilogue per round of workgroups
@@ -112,7 +114,7 @@ struct TileCand { int bm, bn; double eff, pair, eff1; };
 constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 1.0}, {192, 256, 0.95, 0.0, 0.95},
                                 {128, 128, 0.6, 1.26, 0.8}};
 constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 0.85}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0}, {128, 128, 0.5, 1.22, 0.5}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0}, {128, 128, 0.5, 1.22, 0.6}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
 double rounds_factor(const TileCand& t, int64_t wgs) {

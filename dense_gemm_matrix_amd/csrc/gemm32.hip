@@ -14,6 +14,8 @@
 // waves in a 2 x 2 layout, each wave (TB/2)^2 as blocks of 32 x 32 fp32
 // accumulators.
 
+#include <type_traits>
+
 #include "kern_common.h"
 
 namespace dgemm {
@@ -329,7 +331,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 #pragma unroll
     for (int i = 0; i < KB; ++i) voff_b[i] = (kb * KB + i) * ldb * 4 + nb * 16;
 
-    u32x4 ra[2 * AR], rb[KB];
+    // Staging registers: one set at 256 x 256 (the register file is full), two
+    // at 128 x 128, where step kt's loads fetch step kt + 3 into the set that
+    // step kt + 1's pieces have just emptied, three chunk pairs ahead of their
+    // use instead of one (a grid of one workgroup per CU has nothing else to
+    // hide that latency).  Set indices are compile-time: I0 / I1 below.
+    constexpr int NSET = TB == 128 ? 2 : 1;
+    u32x4 ra[NSET][2 * AR], rb[NSET][KB];
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % NSET>;
 
     // Global loads of step kt into registers.  Steps at or past the end get
     // empty ranges and load zeros (the schedule below issues them
@@ -353,25 +363,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
         return StepDesc{make_rsrc(abase, abytes), make_rsrc(bbase, bbytes)};
     };
-    auto load_one = [&](const StepDesc& d, int j) {
+    auto load_one = [&](const StepDesc& d, int j, auto set) {
+        constexpr int P = decltype(set)::value;
         if (j < 2 * AR)
-            ra[j] = load16(d.a, voff_a[j >> 1] + (j & 1) * 16);
+            ra[P][j] = load16(d.a, voff_a[j >> 1] + (j & 1) * 16);
         else
-            rb[j - 2 * AR] = load16(d.b, voff_b[j - 2 * AR]);
+            rb[P][j - 2 * AR] = load16(d.b, voff_b[j - 2 * AR]);
     };
-    auto mask_a = [&](int kt) {
+    auto mask_a = [&](int kt, auto set) {
+        constexpr int P = decltype(set)::value;
         const int valid = K - kt * BK - ac * 8;
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
-            ra[2 * i] = mask_tail32(ra[2 * i], valid);
-            ra[2 * i + 1] = mask_tail32(ra[2 * i + 1], valid - 4);
+            ra[P][2 * i] = mask_tail32(ra[P][2 * i], valid);
+            ra[P][2 * i + 1] = mask_tail32(ra[P][2 * i + 1], valid - 4);
         }
     };
-    auto load_step = [&](int kt, bool tail) {
+    auto load_step = [&](int kt, bool tail, auto set) {
         const StepDesc d = step_desc(kt);
 #pragma unroll
-        for (int j = 0; j < NLOAD; ++j) load_one(d, j);
-        if (tail) mask_a(kt);
+        for (int j = 0; j < NLOAD; ++j) load_one(d, j, set);
+        if (tail) mask_a(kt, set);
     };
 
     // Store unit u (0 .. NU - 1) into stage s: u < AR splits A row ar0 + 64 u
@@ -382,16 +394,17 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     // ul[w]; the last piece writes both parts to LDS.
     uint32_t uh[4], ul[4];
     auto unit_pairs = [](int u) { return u < AR ? 4 : KB / 2; };
-    auto unit_piece = [&](int s, int u, int w) __attribute__((always_inline)) {
+    auto unit_piece = [&](int s, int u, int w, auto set) __attribute__((always_inline)) {
+        constexpr int P = decltype(set)::value;
         if (w < unit_pairs(u)) {
             float x0, x1;
             if (u < AR) {
-                const u32x4& r = ra[2 * u + (w >> 1)];
+                const u32x4& r = ra[P][2 * u + (w >> 1)];
                 x0 = as_float(r[(w & 1) * 2]);
                 x1 = as_float(r[(w & 1) * 2 + 1]);
             } else {
-                x0 = as_float(rb[2 * w][u - AR]);
-                x1 = as_float(rb[2 * w + 1][u - AR]);
+                x0 = as_float(rb[P][2 * w][u - AR]);
+                x1 = as_float(rb[P][2 * w + 1][u - AR]);
             }
             // Empty volatile asm statements pin the split to this point of the
             // schedule: the instruction selector orders them with the
@@ -423,19 +436,19 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     };
     // Pieces in order: unit 0's pairs and write, unit 1's, ...
     constexpr int NPIECE = AR * 5 + 4 * (KB / 2 + 1);
-    auto store_pieces = [&](int s, int p0, int p1) __attribute__((always_inline)) {  // pieces [p0, p1)
+    auto store_pieces = [&](int s, int p0, int p1, auto set) __attribute__((always_inline)) {  // pieces [p0, p1)
 #pragma unroll
         for (int p = p0; p < p1; ++p) {
             constexpr int PB = KB / 2 + 1;  // pieces per B unit
             if (p < AR * 5)
-                unit_piece(s, p / 5, p % 5);
+                unit_piece(s, p / 5, p % 5, set);
             else
-                unit_piece(s, AR + (p - AR * 5) / PB, (p - AR * 5) % PB);
+                unit_piece(s, AR + (p - AR * 5) / PB, (p - AR * 5) % PB, set);
         }
     };
-    auto store_unit = [&](int s, int u) __attribute__((always_inline)) {
+    auto store_unit = [&](int s, int u, auto set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int w = 0; w <= unit_pairs(u); ++w) unit_piece(s, u, w);
+        for (int w = 0; w <= unit_pairs(u); ++w) unit_piece(s, u, w, set);
     };
 
     const int wm = wave >> 1;
@@ -490,63 +503,122 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
     //   pair 1's second half, carrying the NR reads of step kt + 1's pair 0 and
     //   the KB loads of step kt + 2's B (the B pieces have emptied those).
     // Every load is thus issued about NM slots before its first use, and no
-    // slot carries more than two memory instructions.  The last steps also
+    // slot carries more than two memory instructions.  With two staging sets
+    // (128 x 128) the same slots load step kt + 3 into the set step kt + 1's
+    // pieces have just emptied, 2 NM slots earlier than one set allows: 6-12 %
+    // faster on grids of one workgroup per CU (2048^3: 65.5 -> 61.3 us,
+    // 1536 x 1536 x 6144: 179.8 -> 158.8 us), the same results bit for bit.  The last steps also
     // load, split and store steps nk and nk + 1 (empty ranges: zeros, inside
     // the LDS array; never read).
-    auto pieces_at = [&](int s, int slot) __attribute__((always_inline)) {  // the pieces placed after MFMA slot (0 .. 2 NM - 1)
+    auto pieces_at = [&](int s, int slot, auto set) __attribute__((always_inline)) {  // the pieces placed after MFMA slot (0 .. 2 NM - 1)
         const int d = slot - NM / 2;
-        if (d >= 0 && d < NM) store_pieces(s, (d * NPIECE) / NM, ((d + 1) * NPIECE) / NM);
+        if (d >= 0 && d < NM) store_pieces(s, (d * NPIECE) / NM, ((d + 1) * NPIECE) / NM, set);
+    };
+    // One step; `set` holds step kt + 1's loaded values, which this step splits
+    // into stage cur ^ 1, and then receives the loads of step kt + 1 + NSET.
+    auto step = [&](int kt, auto set) __attribute__((always_inline)) {
+        const int cur = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            mfma_one(fa[0], fb[0], i);
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int Q = NM / 2;  // the slots before the first store piece
+            if (i < Q) {
+#pragma unroll
+                for (int r = (i * NR) / Q; r < ((i + 1) * NR) / Q; ++r)
+                    read_one(cur, 1, fa[1], fb[1], r);
+            }
+            if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1, set);
+            pieces_at(cur ^ 1, i, set);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Step kt + 1 + NSET's loads: A's into the registers the A pieces have
+        // just emptied, B's after the barrier.
+        const StepDesc nd = step_desc(kt + 1 + NSET);
+        constexpr int H = NM - NM / 2;
+#pragma unroll
+        for (int i = 0; i < NM / 2; ++i) {
+            mfma_one(fa[1], fb[1], i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int l = (i * 2 * AR) / H; l < ((i + 1) * 2 * AR) / H; ++l) load_one(nd, l, set);
+            pieces_at(cur ^ 1, NM + i, set);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = NM / 2; i < NM; ++i) {
+            mfma_one(fa[1], fb[1], i);
+            __builtin_amdgcn_sched_barrier(0);
+            const int j = i - NM / 2;
+#pragma unroll
+            for (int l = (j * KB) / H; l < ((j + 1) * KB) / H; ++l) load_one(nd, 2 * AR + l, set);
+#pragma unroll
+            for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
+                read_one(cur ^ 1, 0, fa[0], fb[0], r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     if (nk > 0) {
-        load_step(0, ragged_k && nk == 1);
+        load_step(0, ragged_k && nk == 1, I0{});
 #pragma unroll
-        for (int u = 0; u < NU; ++u) store_unit(0, u);
+        for (int u = 0; u < NU; ++u) store_unit(0, u, I0{});
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, fa[0], fb[0], r);
-        load_step(1, false);  // step 1's tail mask, if any, is applied in the loop
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                mfma_one(fa[0], fb[0], i);
+        // Later steps' tail masks, if any, are applied in the loop.
+        load_step(1, false, I1{});
+        if constexpr (NSET == 2) {
+            load_step(2, false, I0{});
+            for (int kt = 0; kt < nk; kt += 2) {
+                step(kt, I1{});
+                if (kt + 1 < nk) step(kt + 1, I0{});
+            }
+        } else {
+            // One set (256 x 256): the same schedule written as a plain loop,
+            // which keeps the compiler's code for this instantiation as it was.
+            for (int kt = 0; kt < nk; ++kt) {
+                const int cur = kt & 1;
                 __builtin_amdgcn_sched_barrier(0);
-                constexpr int Q = NM / 2;  // the slots before the first store piece
-                if (i < Q) {
 #pragma unroll
-                    for (int r = (i * NR) / Q; r < ((i + 1) * NR) / Q; ++r)
-                        read_one(cur, 1, fa[1], fb[1], r);
+                for (int i = 0; i < NM; ++i) {
+                    mfma_one(fa[0], fb[0], i);
+                    __builtin_amdgcn_sched_barrier(0);
+                    constexpr int Q = NM / 2;
+                    if (i < Q) {
+#pragma unroll
+                        for (int r = (i * NR) / Q; r < ((i + 1) * NR) / Q; ++r)
+                            read_one(cur, 1, fa[1], fb[1], r);
+                    }
+                    if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1, I0{});
+                    pieces_at(cur ^ 1, i, I0{});
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                if (i == NM / 2 - 1 && ragged_k && kt + 2 == nk) mask_a(kt + 1);
-                pieces_at(cur ^ 1, i);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // Step kt + 2's loads: A's into the registers the A pieces have just
-            // emptied, B's after the barrier, each about 48 slots before use.
-            const StepDesc nd = step_desc(kt + 2);
-            constexpr int H = NM - NM / 2;
+                const StepDesc nd = step_desc(kt + 2);
+                constexpr int H = NM - NM / 2;
 #pragma unroll
-            for (int i = 0; i < NM / 2; ++i) {
-                mfma_one(fa[1], fb[1], i);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < NM / 2; ++i) {
+                    mfma_one(fa[1], fb[1], i);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int l = (i * 2 * AR) / H; l < ((i + 1) * 2 * AR) / H; ++l) load_one(nd, l);
-                pieces_at(cur ^ 1, NM + i);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            __syncthreads();
+                    for (int l = (i * 2 * AR) / H; l < ((i + 1) * 2 * AR) / H; ++l) load_one(nd, l, I0{});
+                    pieces_at(cur ^ 1, NM + i, I0{});
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();
 #pragma unroll
-            for (int i = NM / 2; i < NM; ++i) {
-                mfma_one(fa[1], fb[1], i);
-                __builtin_amdgcn_sched_barrier(0);
-                const int j = i - NM / 2;
+                for (int i = NM / 2; i < NM; ++i) {
+                    mfma_one(fa[1], fb[1], i);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int j = i - NM / 2;
 #pragma unroll
-                for (int l = (j * KB) / H; l < ((j + 1) * KB) / H; ++l) load_one(nd, 2 * AR + l);
+                    for (int l = (j * KB) / H; l < ((j + 1) * KB) / H; ++l) load_one(nd, 2 * AR + l, I0{});
 #pragma unroll
-                for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
-                    read_one(cur ^ 1, 0, fa[0], fb[0], r);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int r = (j * NR) / H; r < ((j + 1) * NR) / H; ++r)
+                        read_one(cur ^ 1, 0, fa[0], fb[0], r);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
