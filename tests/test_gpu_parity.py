@@ -202,6 +202,24 @@ def test_128_tile_with_either_ring_depth(path, M, N, K):
     assert gap_untouched(C)
 
 
+@pytest.mark.parametrize("K", [1, 31, 32, 33, 64, 95, 96, 97, 150, 160, 191, 200])
+def test_3xbf16_128_tile_step_counts(K):
+    """The 3 x bf16 kernel's 128 x 128 tile stages through two register sets,
+    alternating by step, with each step loading three steps ahead and the K loop
+    unrolled by two.  K from 1 to 200 gives 1 to 7 steps of 32, even and odd
+    counts, with the ragged last step in either set.  Integer inputs (lo parts
+    zero): C is exact and must equal the oracle bit for bit."""
+    M, N = 300, 264
+    tm = dg.dgemm_tile_map(M, N, "f32x3")
+    assert tm["tile_rows"] == 128
+    print(f"case x3-128 K={K}", flush=True)
+    A, B = pair(M, N, K, "ints", "f32", seed=3600 + K)
+    C = run("f32x3", "f32", A, B, a_extra=8, b_extra=8)
+    C64, _ = oracle.gemm("f32", A, B)
+    assert np.array_equal(to64(C), C64)
+    assert gap_untouched(C)
+
+
 @pytest.mark.parametrize("path", ["bf16", "f16"])
 def test_exact_integer_192_tile_freivalds(path):
     """4000 x 3000 x 4104 selects the 192 x 256 macro-tile: integer inputs,
