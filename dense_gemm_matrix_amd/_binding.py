@@ -87,6 +87,11 @@ def _pitch(t: torch.Tensor, row_len: int) -> int:
 
 
 def _shapes(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
+    """(M, N, K) after checking that A, B and C are 2-D, conformable and on one
+    GPU: the library launches on C's device and would otherwise be handed another
+    device's pointers."""
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("operands must be 2-D")
     M, K = A.shape
     K2, N = B.shape
     if K != K2 or tuple(C.shape) != (M, N):
@@ -94,6 +99,8 @@ def _shapes(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
     for t in (A, B, C):
         if t.device.type != "cuda":
             raise ValueError("operands must be device tensors")
+    if not (A.device == B.device == C.device):
+        raise ValueError(f"operands on different devices: {A.device}, {B.device}, {C.device}")
     return M, N, K
 
 
@@ -230,8 +237,14 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, *, bias: torch.Tens
     that block out again only to later work on the same stream, which runs after
     these kernels.  C belongs to that stream too: a caller that goes on to use
     it on another stream orders the two streams (or calls C.record_stream)."""
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("operands must be 2-D")
+    if A.dtype not in _TORCH_IN or B.dtype != A.dtype:
+        raise TypeError(f"unsupported input dtypes {A.dtype}, {B.dtype}")
     if out_dtype is None:
         out_dtype = A.dtype
+    if out_dtype not in (torch.float32, A.dtype):
+        raise TypeError(f"out_dtype must be float32 or {A.dtype}")
     if stream is not None and stream != torch.cuda.current_stream(A.device):
         with torch.cuda.stream(stream):
             return matmul(A, B, out_dtype, bias=bias, relu=relu, alpha=alpha, split_k=split_k)
