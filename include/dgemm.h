@@ -15,13 +15,17 @@
  * window (the ldc - N gap of each row) are never written.
  *
  * Ownership: A, B and C (and gemm_ex's bias and workspace) are DEVICE pointers
- * owned by the caller.  The library allocates no device memory and keeps no
- * pointer after a call returns.
+ * owned by the caller, all in the memory of the calling thread's current HIP
+ * device, and `stream` belongs to that device; the library launches there and
+ * does not check where a pointer lives (a pointer into another GPU's memory is
+ * the caller's error and faults like any bad address).  The library allocates
+ * no device memory and keeps no pointer after a call returns.
  *
  * Execution: each call validates its arguments, enqueues its kernels (one,
  * or two for a split-K plan of gemm_ex) on `stream` (a hipStream_t; NULL
- * means the default stream) and returns without waiting.  Results are visible once the stream has synchronised.  Calls from
- * different host threads on different streams are independent.
+ * means the default stream) and returns without waiting.  Results are visible
+ * once the stream has synchronised.  Calls from different host threads on
+ * different streams are independent.
  *
  * Errors: a non-zero status is returned and NOTHING is enqueued when the
  * arguments are invalid; C is left untouched.  The library never aborts and
