@@ -471,6 +471,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(value / peak, 4), "traffic": traffic},
     }
+    props = torch.cuda.get_device_properties(0)
+    cus = int(props.multi_processor_count)
+    # Dense matrix FLOP per clock per CU on CDNA4: 4 SIMDs x 1024 (bf16/fp16) or
+    # x 64 (fp32); at the 2.4 GHz peak engine clock.
+    per_cu_clk = {"bf16": 4096, "f16": 4096, "f32": 256}[args.dtype]
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                      "compute_units": cus, "hbm_gib": round(props.total_memory / 2**30, 1),
+                      "peak_from_cus_tflops": round(cus * per_cu_clk * 2.4e9 / 1e12, 1),
+                      "peak_used_tflops": peak}
     if not args.no_cold_cache:
         t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
         line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
