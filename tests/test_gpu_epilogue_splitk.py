@@ -281,7 +281,7 @@ def test_full_size_ragged_workload_with_fused_epilogue():
     assert res["ok"], res
 
 
-def random_cases(n=40, seed=6100):
+def random_cases(n=96, seed=6100):
     rng = np.random.default_rng(seed)
     for i in range(n):
         path, out = PATHS[int(rng.integers(len(PATHS)))]
