@@ -7,7 +7,7 @@ that one kernel) on inputs already resident in HBM.  The headline line is the
 bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
 fp32-input 4096^3 products are measured the same way and reported under
 "per_dtype".  Also reported: the same product from a cold cache (each launch
-after a 512 MiB write), torch.matmul (hipBLASLt) on the same inputs for context,
+after a 512 MiB write), with --vendor torch.matmul (hipBLASLt) on the same inputs,
 and the graphics clock and socket power amd-smi reads while the product runs.  The
 other parity workloads, and one GPU's row share of the 4096^3
 product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
@@ -17,7 +17,7 @@ bound by the host's launch rate).
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
-                    [--no-power-clock] [--no-cold-cache] [--no-vendor]
+                    [--no-power-clock] [--no-cold-cache] [--vendor] [--settle-s S]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -92,14 +92,42 @@ def device_inputs(name):
     return A, B, Ad, Bd, Cd, meta
 
 
-def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int):
+def settle_clock(entry, Ad, Bd, Cd, seconds: float) -> int:
+    """Launches back to back for `seconds` of wall time, a few launches queued
+    ahead at most, and returns how many ran.  The chip's clock and power
+    controller take tens of milliseconds to settle after a change of load
+    (right after the inputs are uploaded the first launches run 10-25 % slower
+    than the steady state), so timing starts from a settled clock."""
+    import torch
+    if seconds <= 0:
+        return 0
+    stream = torch.cuda.current_stream()
+    end = time.perf_counter() + seconds
+    n = 0
+    prev = None
+    while time.perf_counter() < end:
+        for _ in range(8):
+            entry(Ad, Bd, Cd, stream=stream)
+        n += 8
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        if prev is not None:
+            prev.synchronize()
+        prev = ev
+    torch.cuda.synchronize()
+    return n
+
+
+def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int, settle_s: float = 0.0):
     """Average kernel duration (s) over `steps` back-to-back launches, timed with
-    HIP events recorded on the stream the library launches on."""
+    HIP events recorded on the stream the library launches on, after `warmup`
+    launches and then `settle_s` seconds of launches."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         entry(Ad, Bd, Cd, stream=stream)
     torch.cuda.synchronize()
+    settle_clock(entry, Ad, Bd, Cd, settle_s)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -133,6 +161,19 @@ def vendor_library(Ad, Bd, steps: int, warmup: int):
     return start.elapsed_time(stop) * 1e-3 / steps
 
 
+def host_cpus() -> dict:
+    """The host's CPU count beside the oracle's thread count: one GPU's share of
+    the host is 16 CPUs, so the oracle runs at most 16 threads however many CPUs
+    the machine shows."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        allowed = os.cpu_count() or 1
+    return {"host_cpus": os.cpu_count(), "host_cpus_allowed": allowed,
+            "cores_rule": "threads = min(16, CPUs this process may use); 16 is one GPU's "
+                          "share of the host"}
+
+
 def cpu_baseline(A, B, meta, target_s: float = 12.0):
     """The oracle, untuned, on a bounded sample of the same product: the first
     r rows of C, r chosen so the timed run takes about target_s seconds; when
@@ -162,7 +203,7 @@ def cpu_baseline(A, B, meta, target_s: float = 12.0):
             total += time.perf_counter() - t0
             reps += 1
         return {"value": round(tflops(M * reps, N, K, total), 6), "unit": "TFLOP/s",
-                "cores": threads, "kind": "oracle",
+                "cores": threads, **host_cpus(), "kind": "oracle",
                 "sample": f"the whole {meta['name']} product ({M}x{N} outputs, K={K}), {reps} "
                           f"times, fp64 triple loop incl. exact widening of B, {total:.1f} s"}
     rows = int(min(M, max(probe, (target_s - fixed) / per_row)))
@@ -171,7 +212,7 @@ def cpu_baseline(A, B, meta, target_s: float = 12.0):
     oracle.gemm(dt, A, B, rows=np.arange(rows), nthreads=threads)
     t = time.perf_counter() - t0
     return {"value": round(tflops(rows, N, K, t), 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, **host_cpus(), "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of C ({rows}x{N} outputs, K={K}) of the "
                       f"{meta['name']} product, fp64 triple loop incl. exact widening of B, "
                       f"{t:.1f} s"}
@@ -382,7 +423,7 @@ def other_shapes(dg, args):
         flop_s = gemm_flops(M, N, K)
         steps = max(10, min(args.steps, int(2e4 * 1e9 / flop_s)))
         warm = max(3, min(args.warmup, steps))
-        t, _ = time_gemm(plain, Ad, Bd, Cd, steps, warm)
+        t, _ = time_gemm(plain, Ad, Bd, Cd, steps, warm, min(args.settle_s, 0.3))
         tg = time_graph(plain, Ad, Bd, Cd, min(steps, 100))
         rec = {"shape": label, "M": M, "N": N, "K": K, "steps": steps,
                "plain_us": round(t * 1e6, 2), "plain_tflops": round(tflops(M, N, K, t), 2),
@@ -395,7 +436,7 @@ def other_shapes(dg, args):
 
             def split_entry(a, b, c, stream=None, ws=ws):
                 dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
-            t2, _ = time_gemm(split_entry, Ad, Bd, Cd, steps, warm)
+            t2, _ = time_gemm(split_entry, Ad, Bd, Cd, steps, warm, min(args.settle_s, 0.3))
             t2g = time_graph(split_entry, Ad, Bd, Cd, min(steps, 100))
             rec["split_us"] = round(t2 * 1e6, 2)
             rec["split_tflops"] = round(tflops(M, N, K, t2), 2)
@@ -418,7 +459,11 @@ def main():
     ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--no-power-clock", action="store_true")
     ap.add_argument("--no-cold-cache", action="store_true")
-    ap.add_argument("--no-vendor", action="store_true", help="skip the torch.matmul comparison")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the same inputs, for context")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of launches after the warm-up before each timed block, "
+                         "so that timing starts from a settled clock (default 1.0)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -443,7 +488,8 @@ def main():
     M, N, K = meta["M"], meta["N"], meta["K"]
     torch.cuda.synchronize()
     print(f"bench: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
-    per_launch, wall = time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, args.warmup)
+    per_launch, wall = time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, args.warmup,
+                                 args.settle_s)
     # Five more timed blocks of the same K steps (no further warm-up), for the
     # spread between trials; `value` stays the first block's.
     trials = [time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, 0)[0] for _ in range(5)]
@@ -465,6 +511,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": DESCRIPTION[name], "M": M, "N": N, "K": K,
                    "frac_of_peak": round(value / peak, 4), "wall_s_timed_region": round(wall, 4),
+                   "settle_s": args.settle_s,
                    "trials_ms_per_step": [round(t * 1e3, 5) for t in trials],
                    "trials_median_ms": round(sorted(trials)[2] * 1e3, 5),
                    "trials_min_ms": round(min(trials) * 1e3, 5)},
@@ -484,7 +531,7 @@ def main():
         t_cold = cold_cache(entry[args.dtype], Ad, Bd, Cd)
         line["cold_cache"] = {"us": round(t_cold * 1e6, 2), "tflops": round(tflops(M, N, K, t_cold), 2),
                               "launches": 20, "how": "each launch after writing a 512 MiB buffer"}
-    if not args.no_vendor:
+    if args.vendor:
         print("bench: timing torch.matmul on the same inputs", file=sys.stderr, flush=True)
         t_v = vendor_library(Ad, Bd, args.steps, min(args.warmup, 50))
         line["vendor_library"] = {
@@ -505,7 +552,8 @@ def main():
             print(f"bench: per-dtype {key} {wn}", file=sys.stderr, flush=True)
             _, _, a2, b2, c2, m2 = device_inputs(wn)
             steps = max(10, args.steps // (8 if key == "f32" else 1))
-            t2, _ = time_gemm(fn, a2, b2, c2, steps, max(3, args.warmup // 4))
+            t2, _ = time_gemm(fn, a2, b2, c2, steps, max(3, args.warmup // 4),
+                              min(args.settle_s, 0.5))
             v2 = tflops(m2["M"], m2["N"], m2["K"], t2)
             peak = PEAK_TFLOPS["bf16"] / 3 if key == "f32_3xbf16" else PEAK_TFLOPS[dt]
             per[key] = {"workload": DESCRIPTION[wn], "value": round(v2, 2), "unit": "TFLOP/s",

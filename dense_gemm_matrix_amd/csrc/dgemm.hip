@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -41,6 +42,42 @@ bool ranges_overlap(uintptr_t a0, int64_t alen, uintptr_t b0, int64_t blen) {
     return a0 < b0 + (uintptr_t)blen && b0 < a0 + (uintptr_t)alen;
 }
 
+// The bytes a row-major operand occupies: `rows` rows of `row_bytes` each,
+// `pitch` bytes apart.  A contiguous range is one row.
+struct Span {
+    uintptr_t base;
+    int64_t rows, row_bytes, pitch;
+};
+
+Span matrix_span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+    return Span{(uintptr_t)p, rows, cols * esize, ld * esize};
+}
+
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+    return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Whether any byte of x's rows is also a byte of y's rows.  With equal pitches
+// (a one-row span takes the other's pitch) row i of x and row j of y overlap
+// iff -x.row_bytes < (x.base - y.base) + (i - j) * pitch < y.row_bytes, which is
+// decided for the t = i - j closest to the upper bound.  With different pitches
+// the two spans are compared from their first to their last byte, which may
+// report an overlap of interleaved rows that share no byte.
+bool spans_overlap(Span x, Span y) {
+    if (x.rows <= 0 || y.rows <= 0 || x.row_bytes <= 0 || y.row_bytes <= 0) return false;
+    const int64_t xlen = (x.rows - 1) * x.pitch + x.row_bytes;
+    const int64_t ylen = (y.rows - 1) * y.pitch + y.row_bytes;
+    if (!ranges_overlap(x.base, xlen, y.base, ylen)) return false;
+    if (x.rows == 1) x.pitch = y.pitch;
+    if (y.rows == 1) y.pitch = x.pitch;
+    if (x.pitch != y.pitch || x.pitch <= 0) return true;
+    const int64_t p = x.pitch;
+    const int64_t d = (int64_t)(x.base - y.base);
+    const int64_t t = std::min(floor_div(y.row_bytes - 1 - d, p), x.rows - 1);
+    if (t < -(y.rows - 1)) return false;
+    return d + t * p > -x.row_bytes;
+}
+
 int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
              int ldc, int in, int es_out) {
     const int es = in_esize(in);
@@ -57,11 +94,9 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
                   ((int64_t)ldb * es) % 16))
         return DGEMM_ERR_MISALIGNED;
     if (reads) {
-        const int64_t alen = ((int64_t)(M - 1) * lda + K) * es;
-        const int64_t blen = ((int64_t)(K - 1) * ldb + N) * es;
-        const int64_t clen = ((int64_t)(M - 1) * ldc + N) * es_out;
-        if (ranges_overlap((uintptr_t)C, clen, (uintptr_t)A, alen) ||
-            ranges_overlap((uintptr_t)C, clen, (uintptr_t)B, blen))
+        const Span c = matrix_span(C, M, N, ldc, es_out);
+        if (spans_overlap(c, matrix_span(A, M, K, lda, es)) ||
+            spans_overlap(c, matrix_span(B, K, N, ldb, es)))
             return DGEMM_ERR_ALIAS;
     }
     // Buffer descriptors address one 256-row panel of A and one K step of B
@@ -332,17 +367,15 @@ int gemm_ex(int in, int out, int M, int N, int K, const void* A, int lda, const 
     if (M == 0 || N == 0) return DGEMM_OK;
     if (bias && ((uintptr_t)bias & 3)) return DGEMM_ERR_MISALIGNED;
     if (workspace_bytes > 0 && ((uintptr_t)workspace & 15)) return DGEMM_ERR_MISALIGNED;
-    const int64_t clen = ((int64_t)(M - 1) * ldc + N) * es_out;
-    if (bias && ranges_overlap((uintptr_t)C, clen, (uintptr_t)bias, (int64_t)N * 4))
-        return DGEMM_ERR_ALIAS;
+    const Span c = matrix_span(C, M, N, ldc, es_out);
+    const Span b = matrix_span(bias, 1, N, N, 4);
+    if (bias && spans_overlap(c, b)) return DGEMM_ERR_ALIAS;
     const Plan p = make_plan(in, es_out, M, N, K, workspace ? workspace_bytes : 0);
     if (p.splits > 1) {
         const int es = in_esize(in);
-        const uintptr_t w = (uintptr_t)workspace;
-        if (ranges_overlap(w, p.ws_bytes, (uintptr_t)C, clen) ||
-            ranges_overlap(w, p.ws_bytes, (uintptr_t)A, ((int64_t)(M - 1) * lda + K) * es) ||
-            ranges_overlap(w, p.ws_bytes, (uintptr_t)B, ((int64_t)(K - 1) * ldb + N) * es) ||
-            (bias && ranges_overlap(w, p.ws_bytes, (uintptr_t)bias, (int64_t)N * 4)))
+        const Span w = matrix_span(workspace, 1, p.ws_bytes, p.ws_bytes, 1);
+        if (spans_overlap(w, c) || spans_overlap(w, matrix_span(A, M, K, lda, es)) ||
+            spans_overlap(w, matrix_span(B, K, N, ldb, es)) || (bias && spans_overlap(w, b)))
             return DGEMM_ERR_ALIAS;
     }
     st = check_device();

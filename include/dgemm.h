@@ -36,7 +36,13 @@
  *   - A, B and C are 16-byte aligned, and every row pitch in bytes
  *     (lda*esize_in, ldb*esize_in, ldc*esize_out) is a multiple of 16;
  *   - lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N);
- *   - C's bytes overlap neither A's nor B's.
+ *   - C's bytes overlap neither A's nor B's.  An operand's bytes are its rows
+ *     (row i: row-length elements from base + i * pitch), not the gaps
+ *     between them.  Operands with the same row pitch in bytes are compared
+ *     row by row, so disjoint column windows of one buffer are accepted;
+ *     with different pitches the library compares each operand's first to
+ *     last byte, so rows that interleave without sharing a byte are still
+ *     reported as DGEMM_ERR_ALIAS.
  * Edge semantics: M == 0 or N == 0 is a no-op; K == 0 writes C = 0 (the empty
  * sum).  Any M, N, K >= 0 is accepted; tiles at the matrix edges read zeros
  * beyond K and never store beyond M or N.

@@ -91,6 +91,56 @@ def test_validation_errors(fn):
 
 
 
+def byte_overlap(base_x, rows_x, row_bytes_x, pitch_x, base_y, rows_y, row_bytes_y, pitch_y):
+    """Brute force: whether two row-strided byte sets share a byte."""
+    xs = set()
+    for i in range(rows_x):
+        xs.update(range(base_x + i * pitch_x, base_x + i * pitch_x + row_bytes_x))
+    for j in range(rows_y):
+        r = range(base_y + j * pitch_y, base_y + j * pitch_y + row_bytes_y)
+        if not xs.isdisjoint(r):
+            return True
+    return False
+
+
+def test_alias_rule_against_brute_force():
+    """C against A (gemm_bf16, bf16 C): with equal row pitches the library
+    decides overlap exactly, row by row, so column windows of one buffer are
+    accepted; with different pitches it compares first-to-last-byte spans.
+    B's pitch is made too large for the 32-bit descriptor range, a check that
+    comes after the alias check: every call returns before any launch, with
+    ALIAS or TOO_LARGE telling the alias decision."""
+    import random
+    rnd = random.Random(77)
+    far_b = 0x6000000000
+    ldb_huge = (1 << 31) // 128 + 8
+    n_exact = 0
+    for trial in range(400):
+        M = rnd.randint(1, 6)
+        K = 8 * rnd.randint(1, 4)
+        N = 8 * rnd.randint(1, 4)
+        lda = max(K, N) + 8 * rnd.randint(0, 5)
+        ldc = lda if trial % 3 else N + 8 * rnd.randint(0, 5)
+        a0 = 0x10000000
+        c0 = a0 + 16 * rnd.randint(-4 * lda // 8, 4 * lda // 8 + 4)
+        st = call("gemm_bf16", M, N, K, a0, lda, far_b, ldb_huge, c0, ldc, out=1)
+        assert st in (dg.DGEMM_ERR_ALIAS, dg.DGEMM_ERR_TOO_LARGE), st
+        exact = byte_overlap(a0, M, 2 * K, 2 * lda, c0, M, 2 * N, 2 * ldc)
+        if lda == ldc or M == 1:
+            want = exact
+            n_exact += 1
+        else:
+            want = a0 < c0 + 2 * ((M - 1) * ldc + N) and c0 < a0 + 2 * ((M - 1) * lda + K)
+        assert (st == dg.DGEMM_ERR_ALIAS) == want, (M, N, K, lda, ldc, c0 - a0)
+    assert n_exact > 200
+    # Two column windows of one buffer X[M, K + N]: A = X[:, :K], C = X[:, K:].
+    M, K, N = 64, 64, 32
+    st = call("gemm_bf16", M, N, K, PA, K + N, far_b, ldb_huge, PA + 2 * K, K + N, out=1)
+    assert st == dg.DGEMM_ERR_TOO_LARGE
+    st = call("gemm_bf16", M, N, K, PA, K + N, far_b, ldb_huge, PA + 2 * K - 16, K + N, out=1)
+    assert st == dg.DGEMM_ERR_ALIAS
+
+
 @pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16"])
 def test_empty_output_is_a_no_op_without_device(fn):
     # M == 0 or N == 0: nothing to write, no device needed, even with NULL pointers.
@@ -172,7 +222,7 @@ def test_gemm_ex_validation_errors(in_fmt):
     assert call_ex(in_fmt, 0, 8, 8, 72, **ok) == dg.DGEMM_ERR_LEADING_DIM
     assert call_ex(in_fmt, 0, 8, 8, 8, **ok, bias=0x40000002) == MIS
     assert call_ex(in_fmt, 0, 8, 8, 8, **ok, ws=0x50000008, ws_bytes=1 << 20) == MIS
-    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, bias=PC + 4 * 8) == ALI   # bias inside C
+    assert call_ex(in_fmt, 0, 8, 8, 8, **ok, bias=PC + 4 * 2) == ALI   # bias inside C's row 0
     assert call_ex(in_fmt, 0, 8, 8, 8, A=PA, lda=ld, B=PB, ldb=ld, C=PA, ldc=ld) == ALI
     # a workspace that a split plan would use, overlapping A
     M, N, K = 64, 64, 1 << 14

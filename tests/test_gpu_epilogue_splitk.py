@@ -259,10 +259,11 @@ def test_workspace_smaller_than_the_best_plan_still_gives_the_product():
 
 def test_full_size_ragged_workload_with_fused_epilogue():
     """4000 x 3000 x 4104 (192 x 256 tiles, ragged in every dimension) with
-    alpha, beta, bias and ReLU, bf16 C: sampled rows against the oracle."""
+    alpha, beta, bias and ReLU, bf16 C: every element against the oracle."""
     from synth_inputs import workload
     A, B, meta = workload("bf16_4000x3000x4104")
     M, N, K = meta["M"], meta["N"], meta["K"]
+    assert dg.gemm_ex_plan("bf16", M, N, K, 0, out_same=True)["tile_rows"] == 192
     rng = np.random.default_rng(5900)
     Cold = draw(rng, (M, N), "normal", "bf16")
     bias = rng.standard_normal(N).astype(np.float32) * 0.1
@@ -271,14 +272,42 @@ def test_full_size_ragged_workload_with_fused_epilogue():
     dg.gemm_ex(Ad, Bd, C, alpha=2.0, beta=-0.5, bias=torch.from_numpy(bias).to("cuda"),
                relu=True)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 191, 192, 2047, 3839, 3840, 3999])
-    C64, S = oracle.gemm("bf16", A, B, rows=rows)
-    E, T = oracle.epilogue(C64, 2.0, -0.5, oracle.widen("bf16", Cold[rows]),
+    C64, S = oracle.gemm("bf16", A, B)
+    E, T = oracle.epilogue(C64, 2.0, -0.5, oracle.widen("bf16", Cold),
                            bias.astype(np.float64), True)
     b = bound_epilogue(E, T, S, 2.0, TOL_MFMA, "bf16")
-    got = to64(C[torch.from_numpy(rows).to("cuda")])
-    res = oracle.check(got, E, S, TOL_MFMA, "bf16", b=b)
+    res = oracle.check(to64(C), E, S, TOL_MFMA, "bf16", b=b)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("path,out", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"),
+                                      ("f16", "f32"), ("f32x3", "f32")])
+@pytest.mark.parametrize("alpha,beta,use_bias,relu", [(0.75, -1.0, True, True),
+                                                      (-1.5, 0.5, False, False)])
+def test_fused_epilogue_on_the_256_tile(path, out, alpha, beta, use_bias, relu):
+    """4096 x 4096 outputs with no workspace run the 256 x 256 instantiations
+    that apply the epilogue in the GEMM kernel itself (split plans apply it in
+    the reduction instead).  K = 200 keeps the oracle quick while giving four K
+    steps with a ragged last one.  Every element of C against the oracle."""
+    M = N = 4096
+    K = 200
+    plan = dg.gemm_ex_plan(path, M, N, K, 0, out_same=(out != "f32"))
+    assert (plan["tile_rows"], plan["tile_cols"], plan["splits"]) == (256, 256, 1), plan
+    print(f"case epi256 {path}->{out} a={alpha} b={beta} bias={use_bias} relu={relu}", flush=True)
+    rng = np.random.default_rng(5950 + PATHS.index((path, out)) + (10 if relu else 0))
+    dtype = store(path)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    Cold = draw(rng, (M, N), "normal", out) if beta != 0.0 else None
+    bias = rng.standard_normal(N).astype(np.float32) if use_bias else None
+    C, _ = run_ex(path, out, A, B, alpha=alpha, beta=beta, Cold=Cold, bias=bias, relu=relu)
+    C64, S = oracle.gemm(dtype, A, B)
+    E, T = oracle.epilogue(C64, alpha, beta, None if Cold is None else oracle.widen(out, Cold),
+                           None if bias is None else bias.astype(np.float64), relu)
+    b = bound_epilogue(E, T, S, alpha, TOL_MFMA, out)
+    res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
+    assert res["ok"], res
+    assert gap_untouched(C)
 
 
 def random_cases(n=96, seed=6100):
