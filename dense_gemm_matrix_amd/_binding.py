@@ -37,6 +37,10 @@ _lib.gemm_ex.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_i
                          _c_int, _c_void_p, _c_int, _c_float, _c_float, _c_void_p, _c_int,
                          _c_void_p, _c_size_t, _c_void_p]
 _lib.gemm_ex.restype = _c_int
+_lib.gemm_ex_static.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_int,
+                                _c_void_p, _c_int, _c_void_p, _c_int, _c_float, _c_float,
+                                _c_void_p, _c_int, _c_size_t, _c_void_p]
+_lib.gemm_ex_static.restype = _c_int
 _lib.gemm_ex_plan.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_size_t, _P, _P, _P,
                               ctypes.POINTER(_c_size_t)]
 _lib.gemm_ex_plan.restype = _c_int
@@ -49,6 +53,8 @@ DGEMM_ERR_ALIAS = 4
 DGEMM_ERR_TOO_LARGE = 5
 DGEMM_ERR_DEVICE = 6
 DGEMM_ERR_LAUNCH = 7
+DGEMM_ERR_SCRATCH_SIZE = 8
+DGEMM_STATIC_SCRATCH_BYTES = 32 << 20
 DGEMM_OUT_F32 = 0
 DGEMM_OUT_SAME = 1
 DGEMM_ACT_NONE = 0
@@ -189,14 +195,8 @@ def gemm_ex_plan(in_fmt: str, M: int, N: int, K: int, workspace_bytes: int,
             "workspace_bytes": used.value}
 
 
-def gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float = 1.0,
-            beta: float = 0.0, bias: torch.Tensor = None, relu: bool = False,
-            workspace: torch.Tensor = None, in_fmt: str = None, stream=None) -> None:
-    """C = act(alpha * A @ B + beta * C + bias) through the library's gemm_ex.
-
-    `workspace` (a device tensor, any dtype) lends scratch memory for a split-K
-    plan; None means no split.  `in_fmt` picks "f32x3" for fp32 data on the
-    3 x bf16 path; by default it follows A's dtype."""
+def _ex_args(A, B, C, bias, in_fmt):
+    """(M, N, K, input code, output code, bias pointer) for gemm_ex and gemm_ex_static."""
     M, N, K = _shapes(A, B, C)
     fmt = in_fmt or _TORCH_IN.get(A.dtype)
     if fmt is None or B.dtype != A.dtype or (fmt == "f32x3" and A.dtype != torch.float32):
@@ -213,13 +213,41 @@ def gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float =
                 or not bias.is_contiguous() or bias.device != C.device:
             raise ValueError("bias must be a contiguous float32 device vector of length N")
         bias_ptr = bias.data_ptr()
+    return M, N, K, IN_CODES[fmt], out, bias_ptr
+
+
+def gemm_ex_static(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float = 1.0,
+                   beta: float = 0.0, bias: torch.Tensor = None, relu: bool = False,
+                   scratch_bytes: int = DGEMM_STATIC_SCRATCH_BYTES, in_fmt: str = None,
+                   stream=None) -> None:
+    """gemm_ex with the library's static device scratch as the split-K workspace
+    (scratch_bytes of it); allocates nothing.  Calls that overlap in time on one
+    GPU share that scratch and must be ordered (one stream)."""
+    M, N, K, code, out, bias_ptr = _ex_args(A, B, C, bias, in_fmt)
+    with _on_device(C):
+        _check(_lib.gemm_ex_static(code, out, M, N, K, A.data_ptr(), _pitch(A, K),
+                                   B.data_ptr(), _pitch(B, N), C.data_ptr(), _pitch(C, N),
+                                   float(alpha), float(beta), bias_ptr,
+                                   DGEMM_ACT_RELU if relu else DGEMM_ACT_NONE,
+                                   int(scratch_bytes), _stream(C, stream)))
+
+
+def gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, alpha: float = 1.0,
+            beta: float = 0.0, bias: torch.Tensor = None, relu: bool = False,
+            workspace: torch.Tensor = None, in_fmt: str = None, stream=None) -> None:
+    """C = act(alpha * A @ B + beta * C + bias) through the library's gemm_ex.
+
+    `workspace` (a device tensor, any dtype) lends scratch memory for a split-K
+    plan; None means no split.  `in_fmt` picks "f32x3" for fp32 data on the
+    3 x bf16 path; by default it follows A's dtype."""
+    M, N, K, code, out, bias_ptr = _ex_args(A, B, C, bias, in_fmt)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         if workspace.device != C.device or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on C's device")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with _on_device(C):
-        _check(_lib.gemm_ex(IN_CODES[fmt], out, M, N, K, A.data_ptr(), _pitch(A, K),
+        _check(_lib.gemm_ex(code, out, M, N, K, A.data_ptr(), _pitch(A, K),
                             B.data_ptr(), _pitch(B, N), C.data_ptr(), _pitch(C, N),
                             float(alpha), float(beta), bias_ptr,
                             DGEMM_ACT_RELU if relu else DGEMM_ACT_NONE, ws_ptr, ws_bytes,

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "dgemm.h"
 #include "dgemm_internal.h"
@@ -327,6 +328,77 @@ int gemm_plain(int in, int M, int N, int K, const void* A, int lda, const void* 
                (hipStream_t)stream);
 }
 
+// Device memory of gemm_ex_static's split-K partials: one array on every GPU
+// the library runs on, kept until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory); it passes the address hipGetSymbolAddress returns for the current
+// device, taken once per device.
+static __device__ __align__(256) char scratch[DGEMM_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[256];
+
+// The current device's copy of `scratch`, or DGEMM_ERR_DEVICE.
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return DGEMM_ERR_DEVICE;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return DGEMM_ERR_DEVICE;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DGEMM_OK;
+}
+
+// gemm_ex's checks, plan and launch.  With `use_static`, the workspace is the
+// static scratch array (workspace_bytes of it), which no caller buffer can
+// overlap.
+int gemm_ex_impl(int in, int out, int M, int N, int K, const void* A, int lda, const void* B,
+                 int ldb, void* C, int ldc, float alpha, float beta, const float* bias, int act,
+                 void* workspace, size_t workspace_bytes, void* stream, bool use_static) {
+    if (in < IN_F32 || in > IN_F32X3) return DGEMM_ERR_INVALID_VALUE;
+    const int of = out_format(in, out);
+    if (of < 0 || (act != DGEMM_ACT_NONE && act != DGEMM_ACT_RELU)) return DGEMM_ERR_INVALID_VALUE;
+    if (!use_static && workspace_bytes > 0 && !workspace) return DGEMM_ERR_INVALID_VALUE;
+    const int es_out = out_esize(of);
+    int st = validate(M, N, K, A, lda, B, ldb, C, ldc, in, es_out);
+    if (st != DGEMM_OK) return st;
+    if (M == 0 || N == 0) return DGEMM_OK;
+    if (bias && ((uintptr_t)bias & 3)) return DGEMM_ERR_MISALIGNED;
+    if (!use_static && workspace_bytes > 0 && ((uintptr_t)workspace & 15))
+        return DGEMM_ERR_MISALIGNED;
+    const Span c = matrix_span(C, M, N, ldc, es_out);
+    const Span b = matrix_span(bias, 1, N, N, 4);
+    if (bias && spans_overlap(c, b)) return DGEMM_ERR_ALIAS;
+    const Plan p = make_plan(in, es_out, M, N, K, (use_static || workspace) ? workspace_bytes : 0);
+    if (p.splits > 1 && !use_static) {
+        const int es = in_esize(in);
+        const Span w = matrix_span(workspace, 1, p.ws_bytes, p.ws_bytes, 1);
+        if (spans_overlap(w, c) || spans_overlap(w, matrix_span(A, M, K, lda, es)) ||
+            spans_overlap(w, matrix_span(B, K, N, ldb, es)) || (bias && spans_overlap(w, b)))
+            return DGEMM_ERR_ALIAS;
+    }
+    st = check_device();
+    if (st != DGEMM_OK) return st;
+    if (use_static) {
+        if (p.splits > 1) {
+            st = static_scratch(&workspace);
+            if (st != DGEMM_OK) return st;
+        } else {
+            workspace = nullptr;
+            workspace_bytes = 0;
+        }
+    }
+    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{alpha, beta, bias, act}, workspace,
+               workspace_bytes, (hipStream_t)stream);
+}
+
 }  // namespace
 }  // namespace dgemm
 
@@ -357,31 +429,16 @@ int gemm_f16(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 int gemm_ex(int in, int out, int M, int N, int K, const void* A, int lda, const void* B, int ldb,
             void* C, int ldc, float alpha, float beta, const float* bias, int act,
             void* workspace, size_t workspace_bytes, void* stream) {
-    if (in < IN_F32 || in > IN_F32X3) return DGEMM_ERR_INVALID_VALUE;
-    const int of = out_format(in, out);
-    if (of < 0 || (act != DGEMM_ACT_NONE && act != DGEMM_ACT_RELU)) return DGEMM_ERR_INVALID_VALUE;
-    if (workspace_bytes > 0 && !workspace) return DGEMM_ERR_INVALID_VALUE;
-    const int es_out = out_esize(of);
-    int st = validate(M, N, K, A, lda, B, ldb, C, ldc, in, es_out);
-    if (st != DGEMM_OK) return st;
-    if (M == 0 || N == 0) return DGEMM_OK;
-    if (bias && ((uintptr_t)bias & 3)) return DGEMM_ERR_MISALIGNED;
-    if (workspace_bytes > 0 && ((uintptr_t)workspace & 15)) return DGEMM_ERR_MISALIGNED;
-    const Span c = matrix_span(C, M, N, ldc, es_out);
-    const Span b = matrix_span(bias, 1, N, N, 4);
-    if (bias && spans_overlap(c, b)) return DGEMM_ERR_ALIAS;
-    const Plan p = make_plan(in, es_out, M, N, K, workspace ? workspace_bytes : 0);
-    if (p.splits > 1) {
-        const int es = in_esize(in);
-        const Span w = matrix_span(workspace, 1, p.ws_bytes, p.ws_bytes, 1);
-        if (spans_overlap(w, c) || spans_overlap(w, matrix_span(A, M, K, lda, es)) ||
-            spans_overlap(w, matrix_span(B, K, N, ldb, es)) || (bias && spans_overlap(w, b)))
-            return DGEMM_ERR_ALIAS;
-    }
-    st = check_device();
-    if (st != DGEMM_OK) return st;
-    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{alpha, beta, bias, act}, workspace,
-               workspace_bytes, (hipStream_t)stream);
+    return gemm_ex_impl(in, out, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, act, workspace,
+                        workspace_bytes, stream, false);
+}
+
+int gemm_ex_static(int in, int out, int M, int N, int K, const void* A, int lda, const void* B,
+                   int ldb, void* C, int ldc, float alpha, float beta, const float* bias, int act,
+                   size_t scratch_bytes, void* stream) {
+    if (scratch_bytes > DGEMM_STATIC_SCRATCH_BYTES) return DGEMM_ERR_SCRATCH_SIZE;
+    return gemm_ex_impl(in, out, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, bias, act, nullptr,
+                        scratch_bytes, stream, true);
 }
 
 int gemm_ex_plan(int in, int out, int M, int N, int K, size_t workspace_bytes, int* tile_rows,
@@ -408,6 +465,9 @@ const char* dgemm_status_string(int status) {
     case DGEMM_ERR_TOO_LARGE: return "DGEMM_ERR_TOO_LARGE: a panel exceeds the 32-bit buffer range";
     case DGEMM_ERR_DEVICE: return "DGEMM_ERR_DEVICE: no gfx950 device is current";
     case DGEMM_ERR_LAUNCH: return "DGEMM_ERR_LAUNCH: the kernel launch failed";
+    case DGEMM_ERR_SCRATCH_SIZE:
+        return "DGEMM_ERR_SCRATCH_SIZE: scratch_bytes exceeds the static scratch array "
+               "(DGEMM_STATIC_SCRATCH_BYTES)";
     default: return "DGEMM: unknown status";
     }
 }

@@ -65,7 +65,8 @@ typedef enum {
     DGEMM_ERR_ALIAS = 4,         /* C overlaps A, B or the bias; the workspace overlaps any of them */
     DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 128*ldb bytes reach 2 GiB (32-bit offsets)  */
     DGEMM_ERR_DEVICE = 6,        /* no current device, or it is not a gfx950                     */
-    DGEMM_ERR_LAUNCH = 7         /* the kernel launch reported an error                          */
+    DGEMM_ERR_LAUNCH = 7,        /* the kernel launch reported an error                          */
+    DGEMM_ERR_SCRATCH_SIZE = 8   /* gemm_ex_static: scratch_bytes > DGEMM_STATIC_SCRATCH_BYTES   */
 } dgemm_status;
 
 /* Format of C for the 16-bit entry points. */
@@ -181,6 +182,35 @@ int gemm_ex(int in, int out, int M, int N, int K,
             float alpha, float beta, const float* bias, int act,
             void* workspace, size_t workspace_bytes,
             void* stream);
+
+/* Bytes of the static device array that gemm_ex_static uses as its workspace. */
+#define DGEMM_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * gemm_ex for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  It
+ * computes exactly what gemm_ex computes with a workspace of scratch_bytes,
+ * and the split-K partials go to a static device array of
+ * DGEMM_STATIC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing; the caller
+ * passes A, B, C and bias as for gemm_ex.  scratch_bytes (0 ..
+ * DGEMM_STATIC_SCRATCH_BYTES) bounds the plan as gemm_ex's workspace_bytes
+ * does: gemm_ex_plan(..., scratch_bytes, ...) reports the plan, and 0 never
+ * splits.  A larger value returns DGEMM_ERR_SCRATCH_SIZE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array, and no part of it
+ * needs to start at zero (every partial is written before it is read): calls
+ * whose kernels overlap in time on one GPU (different streams, or different
+ * host threads without ordering) race on it and must be ordered by the
+ * caller, e.g. by issuing them on one stream.  The array's address is looked
+ * up on a device's first call.
+ */
+int gemm_ex_static(int in, int out, int M, int N, int K,
+                   const void* A, int lda,
+                   const void* B, int ldb,
+                   void* C, int ldc,
+                   float alpha, float beta, const float* bias, int act,
+                   size_t scratch_bytes,
+                   void* stream);
 
 /*
  * Host-side query of the plan gemm_ex would use with `workspace_bytes`

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("gemm_f32", "gemm_f32_3xbf16", "gemm_bf16", "gemm_f16", "gemm_ex",
-                 "gemm_ex_plan", "dgemm_status_string", "dgemm_tile_map"):
+                 "gemm_ex_static", "gemm_ex_plan", "dgemm_status_string", "dgemm_tile_map"):
         assert want in names
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     seen = set()
-    for s in range(8):
+    for s in range(9):
         msg = dg.dgemm_status_string(s)
         assert msg.startswith("DGEMM_") and msg not in seen
         seen.add(msg)
@@ -138,6 +138,26 @@ def test_alias_rule_against_brute_force():
     st = call("gemm_bf16", M, N, K, PA, K + N, far_b, ldb_huge, PA + 2 * K, K + N, out=1)
     assert st == dg.DGEMM_ERR_TOO_LARGE
     st = call("gemm_bf16", M, N, K, PA, K + N, far_b, ldb_huge, PA + 2 * K - 16, K + N, out=1)
+    assert st == dg.DGEMM_ERR_ALIAS
+
+
+def test_static_scratch_size_and_its_limit():
+    """The binding's constant is the header's, and a budget beyond the static
+    array is rejected before anything else (no device needed)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define DGEMM_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == dg.DGEMM_STATIC_SCRATCH_BYTES
+    lib = dg.raw()
+    st = lib.gemm_ex_static(1, 0, 8, 8, 8, V(PA), 64, V(PB), 64, V(PC), 64, ctypes.c_float(1.0),
+                            ctypes.c_float(0.0), None, 0, dg.DGEMM_STATIC_SCRATCH_BYTES + 1, None)
+    assert st == dg.DGEMM_ERR_SCRATCH_SIZE
+    assert "DGEMM_STATIC_SCRATCH_BYTES" in dg.dgemm_status_string(st)
+    # otherwise the same validation as gemm_ex, before any device call
+    st = lib.gemm_ex_static(1, 0, 8, 8, 72, V(PA), 64, V(PB), 64, V(PC), 64, ctypes.c_float(1.0),
+                            ctypes.c_float(0.0), None, 0, 0, None)
+    assert st == dg.DGEMM_ERR_LEADING_DIM
+    st = lib.gemm_ex_static(1, 0, 8, 8, 8, V(PA), 64, V(PB), 64, V(PA), 64, ctypes.c_float(1.0),
+                            ctypes.c_float(0.0), None, 0, 1 << 20, None)
     assert st == dg.DGEMM_ERR_ALIAS
 
 
