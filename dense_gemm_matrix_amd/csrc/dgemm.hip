@@ -100,9 +100,11 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
             spans_overlap(c, matrix_span(B, K, N, ldb, es)))
             return DGEMM_ERR_ALIAS;
     }
-    // Buffer descriptors address one 256-row panel of A and one K step of B
-    // (64 rows of 16-bit data, 32 of fp32) with 32-bit offsets.
-    if ((int64_t)PANEL_ROWS * lda * es >= DESC_LIMIT || (int64_t)bk_of(in) * ldb * es >= DESC_LIMIT)
+    // Buffer descriptors address one 256-row panel of A, one K step of B (64
+    // rows of 16-bit data, 32 of fp32) and one 256-row panel of C with 32-bit
+    // offsets.
+    if ((int64_t)PANEL_ROWS * lda * es >= DESC_LIMIT || (int64_t)bk_of(in) * ldb * es >= DESC_LIMIT ||
+        (int64_t)PANEL_ROWS * ldc * es_out >= DESC_LIMIT)
         return DGEMM_ERR_TOO_LARGE;
     return DGEMM_OK;
 }
@@ -237,6 +239,7 @@ Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail) {
             if (tiles * s > INT32_MAX) continue;
             const int64_t ws = (int64_t)s * M * ldw * 4;
             if ((uint64_t)ws > ws_avail) continue;
+            if ((int64_t)PANEL_ROWS * ldw * 4 >= DESC_LIMIT) continue;  // partials' panel limit
             const double us = estimate_us(in, es_out, M, N, cands[c], s, steps, ldw);
             if (us < best) {
                 best = us;

@@ -57,7 +57,7 @@ struct EpiArgs {
 // splits = 1 and kchunk = K.
 struct GemmLaunch {
     int in, out, tbm, tbn;
-    int stages;  // LDS stages of the 16-bit kernel's ring (2, or 4 at 128 x 128)
+    int stages;  // LDS stages of the 16-bit kernel's 128 x 128 tile (2, or 4 alone on a CU)
     bool epi;    // apply `e` in the kernel (only with splits == 1)
     const char* A;
     const char* B;

@@ -1,78 +1,97 @@
 // gemm16.hip -- the bf16 / fp16 GEMM kernel for gfx950 (MI355X).
 //
 // Both operands go global -> LDS with direct-to-LDS buffer loads (no VGPR
-// staging, no LDS write instructions) into a ring of S stages of BK16 = 64-deep
-// slabs, each issued S - 1 steps before its use.  S = 2 for the 256-wide tiles
-// (of the settings that fit 160 KiB, measured fastest; 4 x 32 and 5 x 32 deep
-// were slower).  The 128 x 128 tile has both S = 2 (64 KiB: two workgroups per
-// CU, each hiding the other's load latency) and S = 4 (128 KiB: one workgroup
-// per CU, loads issued three steps ahead); the planner takes S = 4 when the
-// grid has no more workgroups than CUs.  A is stored K-contiguous and read with ds_read_b128.  B is stored as it
-// lies in memory (row-major, N-contiguous) and read with ds_read_b64_tr_b16:
-// within each 16-lane group that instruction performs a 4 x 4 transpose of
-// 4-element row pieces, which hands every lane the four consecutive k of one
-// column that the matrix instruction's B operand needs.
+// staging, no LDS write instructions).  A is staged in slabs of BKA = 64 k, so
+// that every A row piece a load fetches is one 128-byte cache line (64-byte
+// pieces measured 1.5x the L1 -> L2 read requests and twice the L1's
+// pending-request stalls), stored K-contiguous and read with ds_read_b128.  B
+// is stored as it lies in memory (row-major, N-contiguous) and read with
+// ds_read_b64_tr_b16: within each 16-lane group that instruction performs a
+// 4 x 4 transpose of 4-element row pieces, which hands every lane the four
+// consecutive k of one column that the matrix instruction's B operand needs.
 // v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulators.
+//
+// Two schedules of the K loop, chosen per macro-tile by what measured faster:
+//   SLAB2 (256 x 256, 128 x 128): steps of 64 k; a ring of S stages of A and
+//     B (S = 2, or 4 for the 128 x 128 tile alone on its CU) with one barrier
+//     per step, placed after half of the step's matrix instructions; the next
+//     stage's loads go out in the second half.  The 256 x 256 tile runs at the
+//     board's power limit, where this schedule measured 4-5 % faster than RING.
+//   RING (192 x 256): steps of 32 k; SA = 3 A slabs and SB = 2 SA - 2 = 4 B
+//     stages of 32 k-rows (136 KiB), a barrier at the top of each step, and
+//     each step's loads (half an A slab and a B stage, SB - 1 steps ahead)
+//     spread evenly over all of the step's matrix instructions.  That tile is
+//     not power-limited, and there this schedule measured 3-4 % faster.
 //
 // Per workgroup as launched: 256 threads = 4 waves of 64 lanes in a 2 x 2
 // layout, one wave per SIMD, each wave owning a (TBM/2) x (TBN/2) sub-tile held
 // as blocks of 32 x 32 accumulators (256 fp32 per lane at 256 x 256,
-// register-resident for the whole K loop).  The template also builds a 2 x 4
-// layout of 8 waves (two per SIMD), which measured slower at 4096^3.  LDS rows are split into 16-byte chunks whose positions are
-// XORed with a function of the row, so every 16-byte access stays aligned (the
-// principle of the sgemm tf32 page's section 3 swizzles and the hgemm page's
-// section 2) while the access patterns used here hit distinct LDS banks.  The
-// bijective workgroup -> tile map keeps each XCD's workgroups on a compact
-// block of tiles (the sgemm tf32 page's section 4 Grid Swizzling, adapted to 8
-// XCDs with private L2s).  Buffer loads use per-step resource descriptors:
-// rows past M (A) and past K (B) fall outside the range and read as zero, A's
-// K tail is forced to exact zeros, and the epilogue stores only inside M x N;
-// no host padding (the nine-levels tutorial's sections 2.9 and 6.1 offer
-// padding or predication; predication is chosen).
+// register-resident for the whole K loop).  LDS rows are split into 16-byte
+// chunks whose positions are XORed with a function of the row, so every
+// 16-byte access stays aligned (the principle of the sgemm tf32 page's
+// section 3 swizzles and the hgemm page's section 2) while the access patterns
+// used here hit distinct LDS banks.  The bijective workgroup -> tile map keeps
+// each XCD's workgroups on a compact block of tiles (the sgemm tf32 page's
+// section 4 Grid Swizzling, adapted to 8 XCDs with private L2s).  Buffer loads
+// use per-stage resource descriptors: rows past M (A) and past K (B) fall
+// outside the range and read as zero, A's K tail is forced to exact zeros, and
+// the epilogue stores only inside M x N; no host padding (the nine-levels
+// tutorial's sections 2.9 and 6.1 offer padding or predication; predication
+// is chosen).
 //
 // Matrix instructions' internal k order is not observable through the ABI: a
 // lane group's operand carries the same k indices for A and for B, so any
 // permutation of k inside an instruction cancels.
+
+#include <type_traits>
 
 #include "kern_common.h"
 
 namespace dgemm {
 namespace {
 
-constexpr int BK16 = 64;                       // K per stage
-constexpr int KP16 = BK16 / 16;                // 16-k chunk pairs per stage
-constexpr int A16_CH = BK16 / 8;               // 16-byte chunks per A row
-constexpr int A16_ROW = BK16 * 2;              // bytes per staged A row
+constexpr int BKA = 64;                        // K per A slab
+constexpr int A16_CH = BKA / 8;                // 16-byte chunks per A row
+constexpr int A16_ROW = BKA * 2;               // bytes per staged A row
 constexpr int A16_RPB = 1024 / A16_ROW;        // A rows per 1 KiB load block
 
-// Macro-tile TBM x TBN, 2 x WN waves (WN = 2: 4 waves, one per SIMD; WN = 4:
-// 8 waves, two per SIMD), each wave (TBM/2) x (TBN/WN) = MI x NJ blocks of
-// 32 x 32 accumulators, and an LDS ring of S stages.
-template <int TBM, int TBN, int WN = 2, int S_ = 2>
+enum Sched16 { SLAB2 = 0, RING = 1 };
+
+// Macro-tile TBM x TBN, 4 waves in a 2 x 2 layout, each wave (TBM/2) x (TBN/2)
+// = MI x NJ blocks of 32 x 32 accumulators.  SLAB2: SA stages of 64 k of both
+// operands.  RING: SA A slabs of 64 k and SB = 2 SA - 2 B stages of 32 k.
+template <int TBM, int TBN, int SCHED, int SA_>
 struct Tile16 {
-    static constexpr int S = S_;                         // LDS stages
-    static constexpr int NW = 2 * WN;                    // waves
-    static constexpr int NT = 64 * NW;                   // threads
+    static constexpr bool R = SCHED == RING;
+    static constexpr int SA = SA_;                       // A slabs
+    static constexpr int SB = R ? 2 * SA - 2 : SA;       // B stages
+    static constexpr int STEPK = R ? 32 : 64;            // K per loop step (= per B stage)
+    static constexpr int KP = STEPK / 16;                // 16-k chunk pairs per step
+    static constexpr int NW = 4;                         // waves
     static constexpr int MI = TBM / 64;
-    static constexpr int NJ = TBN / (32 * WN);
-    static constexpr int A_STAGE = TBM * A16_ROW;        // bytes per A stage
+    static constexpr int NJ = TBN / 64;
+    static constexpr int A_STAGE = TBM * A16_ROW;        // bytes per A slab
     static constexpr int B_ROW = TBN * 2;                // bytes per staged B row
     static constexpr int B_CH = TBN / 8;                 // 16-byte chunks per B row
-    static constexpr int B_STAGE = BK16 * B_ROW;         // bytes per B stage
+    static constexpr int B_STAGE = STEPK * B_ROW;        // bytes per B stage
     static constexpr int B_RPB = 1024 / B_ROW;           // B rows per 1 KiB load block
-    static constexpr int A_DMA = A_STAGE / 1024 / NW;    // direct-to-LDS loads per wave per stage
-    static constexpr int B_DMA = B_STAGE / 1024 / NW;
+    static constexpr int AH = R ? 2 : 1;                 // steps that load one A slab
+    static constexpr int A_DMA = A_STAGE / 1024 / NW / AH;  // A loads per wave per step
+    static constexpr int B_DMA = B_STAGE / 1024 / NW;       // B loads per wave per step
     static constexpr int LOADS = A_DMA + B_DMA;
     static constexpr int NREAD = MI + 2 * NJ;            // fragment reads per chunk pair
     static constexpr int NMFMA = MI * NJ;                // MFMAs per chunk pair
-    static_assert(TBM % 64 == 0 && TBN % (32 * WN) == 0 && TBM <= NT, "tile shape");
-    static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0,
+    static constexpr int LDS = SA * A_STAGE + SB * B_STAGE;
+    static_assert(TBM % 64 == 0 && TBN % 64 == 0 && TBM <= 64 * NW, "tile shape");
+    static_assert(A_STAGE % (1024 * NW * AH) == 0 && B_STAGE % (1024 * NW) == 0,
                   "whole load blocks per wave");
-    static_assert(S * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
-    static_assert(S >= 2 && (S - 1) * LOADS <= 63, "stages, vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(R ? (SA >= 3 && (2 * SA - 4) * LOADS <= 63) : (SA >= 2 && (SA - 1) * LOADS <= 63),
+                  "stages, vmcnt range");
+    static_assert(NREAD <= 15, "lgkmcnt range");
 };
 
-// Byte offset of chunk c (0..7) of A row r in a stage.  ds_read_b128 serves
+// Byte offset of chunk c (0..7) of A row r in a slab.  ds_read_b128 serves
 // groups of 4 consecutive lanes from a 64-byte window of banks (measured on
 // gfx950 with SQ_LDS_BANK_CONFLICT), and the 4 lanes of a group read 4
 // consecutive rows at one chunk: a16_phi gives those rows 4 distinct slots.
@@ -89,12 +108,13 @@ __device__ __forceinline__ int b16_off(int k, int chunk, int row_bytes) {
     return k * row_bytes + ((chunk ^ b16_swz(k)) << 4);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN, int S>
-__global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
+template <int IN, int OUT, int TBM, int TBN, bool EPI, bool PAIRS, int SCHED, int S>
+__global__ __launch_bounds__(256) void gemm16_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
     int kchunk, int64_t c_zstride, EpiArgs epi) {
-    using T = Tile16<TBM, TBN, WN, S>;
+    using T = Tile16<TBM, TBN, SCHED, S>;
+    constexpr bool RINGS = T::R;
     // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
     // and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when unsplit).
     {
@@ -106,9 +126,9 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
         K = (K - kbeg) < kchunk ? (K - kbeg) : kchunk;
     }
     constexpr int MI = T::MI, NJ = T::NJ;
-    __shared__ __attribute__((aligned(1024))) char smem[T::S * (T::A_STAGE + T::B_STAGE)];
+    __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
     char* const smA = smem;
-    char* const smB = smem + T::S * T::A_STAGE;
+    char* const smB = smem + T::SA * T::A_STAGE;
 
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -119,20 +139,24 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
     const int n0 = tn * TBN;
     const int rows_a = (M - m0) < TBM ? (M - m0) : TBM;
     const int cols_b = (N - n0) < TBN ? (N - n0) : TBN;
-    const int nk = (K + BK16 - 1) / BK16;
+    const int nk = (K + T::STEPK - 1) / T::STEPK;   // loop steps
 
     // Each direct-to-LDS instruction fills a 1 KiB block lane-linearly (lane l
     // -> bytes 16 l .. 16 l + 15), so the swizzle is applied on the global side:
-    // lane l fetches the chunk that belongs in its slot.  Wave w fills the
-    // blocks w * DMA .. (w + 1) * DMA - 1 of each operand's stage: for A,
-    // A16_RPB rows of A16_CH chunks each; for B, B_RPB k-rows of B_CH chunks.
-    int voffA[T::A_DMA], voffB[T::B_DMA];
+    // lane l fetches the chunk that belongs in its slot.  An A slab's blocks are
+    // A16_RPB rows of A16_CH chunks; wave w fills blocks AH w A_DMA ..
+    // AH (w + 1) A_DMA - 1 (under RING half of them, h = 0, 1, in each of the
+    // two steps that load the slab).  A B stage's blocks are B_RPB k-rows of
+    // B_CH chunks; wave w fills blocks w B_DMA .. (w + 1) B_DMA - 1.
+    int voffA[T::AH][T::A_DMA], voffB[T::B_DMA];
 #pragma unroll
-    for (int j = 0; j < T::A_DMA; ++j) {
-        const int rowA = (wave * T::A_DMA + j) * A16_RPB + lane / A16_CH;
-        const int cA = (lane % A16_CH) ^ a16_phi(rowA);
-        voffA[j] = rowA * lda * 2 + cA * 16;
-    }
+    for (int h = 0; h < T::AH; ++h)
+#pragma unroll
+        for (int j = 0; j < T::A_DMA; ++j) {
+            const int rowA = ((T::AH * wave + h) * T::A_DMA + j) * A16_RPB + lane / A16_CH;
+            const int cA = (lane % A16_CH) ^ a16_phi(rowA);
+            voffA[h][j] = rowA * lda * 2 + cA * 16;
+        }
 #pragma unroll
     for (int j = 0; j < T::B_DMA; ++j) {
         const int kB = (wave * T::B_DMA + j) * T::B_RPB + lane / T::B_CH;
@@ -140,50 +164,49 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
         voffB[j] = kB * ldb * 2 + cB * 16;
     }
 
-    // Global loads of step kt into LDS stage kt % S, one instruction at a
-    // time: stage_desc computes the step's two descriptors, dma_one(j) issues
-    // load j (A loads first, then B).  Steps past the end get empty ranges
-    // (they only keep the per-step load count uniform).
-    struct StageDesc { __amdgpu_buffer_rsrc_t ra, rb; int s; };
-    auto stage_desc = [&](int kt) {
-        StageDesc d;
-        d.s = kt % T::S;
-        const int k0 = kt * BK16;
-        const int krem = K - k0;
-        const char* abase = A + ((int64_t)m0 * lda + k0) * 2;
-        const int64_t abytes = krem > 0 ? ((int64_t)(rows_a - 1) * lda + krem) * 2 : 0;
+    // Descriptors and ring slots of A slab v and B stage j.  Slabs and stages
+    // past the end get empty ranges (their loads keep the per-step load count
+    // uniform and fill zeros).  dma_one(j) issues load j of a step (A loads
+    // first, then B); h (which half of the A slab, RING) is a compile-time
+    // constant at every call, so voffA is indexed statically.
+    struct LoadDesc { __amdgpu_buffer_rsrc_t ra, rb; int sa, sb; };
+    auto load_desc = [&](int v, int j) {
+        LoadDesc d;
+        d.sa = v % T::SA;
+        d.sb = (j + T::SB) % T::SB;
+        const int ka = v * BKA;
+        const int krem_a = K - ka;
+        const char* abase = A + ((int64_t)m0 * lda + ka) * 2;
+        const int64_t abytes =
+            krem_a > 0 ? ((int64_t)(rows_a - 1) * lda + (krem_a < BKA ? krem_a : BKA)) * 2 : 0;
         d.ra = make_rsrc(abase, abytes);
-        const int rows_b = krem < BK16 ? krem : BK16;
-        const char* bbase = B + ((int64_t)k0 * ldb + n0) * 2;
+        const int kb = j * T::STEPK;
+        const int rows_b = (K - kb) < T::STEPK ? (K - kb) : T::STEPK;
+        const char* bbase = B + ((int64_t)kb * ldb + n0) * 2;
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 2 : 0;
         d.rb = make_rsrc(bbase, bbytes);
         return d;
     };
-    auto dma_one = [&](const StageDesc& d, int j) {
+    auto dma_one = [&](const LoadDesc& d, int h, int j) {
         if (j < T::A_DMA) {
-            dma16(d.ra, lds_addr(smA + d.s * T::A_STAGE + (wave * T::A_DMA + j) * 1024), voffA[j]);
+            const int blk = (T::AH * wave + h) * T::A_DMA + j;
+            dma16(d.ra, lds_addr(smA + d.sa * T::A_STAGE + blk * 1024), voffA[h][j]);
         } else {
             const int jb = j - T::A_DMA;
-            dma16(d.rb, lds_addr(smB + d.s * T::B_STAGE + (wave * T::B_DMA + jb) * 1024), voffB[jb]);
+            dma16(d.rb, lds_addr(smB + d.sb * T::B_STAGE + (wave * T::B_DMA + jb) * 1024), voffB[jb]);
         }
     };
-    auto issue_stage = [&](int kt) {
-        const StageDesc d = stage_desc(kt);
-#pragma unroll
-        for (int j = 0; j < T::LOADS; ++j) dma_one(d, j);
-    };
 
-    // When K is not a multiple of BK16, the last stage's A columns at and past
-    // K hold other data (row padding, the next row, or zeros past the range);
+    // When K is not a multiple of BKA, the last A slab's columns at and past K
+    // hold other data (row padding, the next row, or zeros past the range);
     // zero them in LDS so that 0 * (NaN or Inf) can never reach the sum.  B's
     // rows past K are already zero (outside the descriptor's range).
+    const int last_slab = (K - 1) / BKA;
     auto fix_tail = [&]() {
-        const int kt = nk - 1;
-        const int s = kt % T::S;
-        const int kin = K - kt * BK16;       // valid k in the last stage, 1..BK16-1
-        const int chunk0 = kin >> 3;         // first chunk holding an invalid element
-        char* rowp = smA + s * T::A_STAGE;
-        const int row = tid;                 // one A row per thread
+        const int kin = K - last_slab * BKA;  // valid k in the last slab, 1..BKA-1
+        const int chunk0 = kin >> 3;          // first chunk holding an invalid element
+        char* rowp = smA + (last_slab % T::SA) * T::A_STAGE;
+        const int row = tid;                  // one A row per thread
         if (row < TBM) {
             if (kin & 7) {
                 short* p = (short*)(rowp + a16_off(row, chunk0));
@@ -194,8 +217,8 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
         }
     };
 
-    const int wm = wave / WN;
-    const int wn = wave % WN;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
     const int g = lane >> 5;          // lane group: k half of a 16-k chunk pair
     const int li = lane & 31;         // row of A within a 32-row block
     const int ta = (lane >> 2) & 3;   // transpose read: source k row within the group
@@ -210,24 +233,31 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
-    // Operand fragments, one register set per chunk pair of a step: A as
-    // MI x 8 consecutive k of a row; B as NJ x (two transpose reads of 4
-    // consecutive k of a column).
-    u32x4 fa[KP16][MI];
-    s16x4 fb[KP16][NJ][2];
+    // Operand fragments, one register set per chunk pair of a step (SLAB2) or
+    // two sets that the pairs alternate between (RING): A as MI x 8
+    // consecutive k of a row; B as NJ x (two transpose reads of 4 consecutive
+    // k of a column).
+    constexpr int NSET = RINGS ? 2 : T::KP;
+    u32x4 fa[NSET][MI];
+    s16x4 fb[NSET][NJ][2];
 
-    // Fragment read number i (0 .. NREAD - 1) of pair kp of step kt: MI A
-    // reads, then 2 NJ B transpose reads (nj = (i - MI) / 2, half (i - MI) % 2).
-    auto read_piece = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2], int i) {
-        if (i < MI) {
-            const char* sa = smA + (kt % T::S) * T::A_STAGE;
-            a[i] = *(const u32x4*)(sa + a16_off(wm * (TBM / 2) + i * 32 + li, 2 * kp + g));
+    // Fragment read number o (0 .. NREAD - 1) of chunk pair kp of step kt, in
+    // the order the matrix instructions first use them: A block 0, the NJ B
+    // blocks (two transpose reads each), then A blocks 1 .. MI - 1.  Under
+    // RING, h = kt & 1 picks the half of the A slab (a compile-time constant).
+    auto read_piece = [&](int kt, int h, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2], int o) {
+        if (o == 0 || o > 2 * NJ) {
+            const int mi = o == 0 ? 0 : o - 2 * NJ;
+            const int slab = RINGS ? (kt >> 1) : kt;
+            const char* sa = smA + (slab % T::SA) * T::A_STAGE;
+            a[mi] = *(const u32x4*)(sa + a16_off(wm * (TBM / 2) + mi * 32 + li,
+                                                 (RINGS ? 4 * h : 0) + 2 * kp + g));
         } else {
-            const char* sb = smB + (kt % T::S) * T::B_STAGE;
-            const int nj = (i - MI) >> 1, h = (i - MI) & 1;
-            const int k = kp * 16 + 8 * g + 4 * h + ta;
-            const int c = wn * (TBN / WN / 8) + nj * 4 + 2 * tg + (tq >> 1);
-            b[nj][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            const char* sb = smB + (kt % T::SB) * T::B_STAGE;
+            const int nj = (o - 1) >> 1, hh = (o - 1) & 1;
+            const int k = kp * 16 + 8 * g + 4 * hh + ta;
+            const int c = wn * (TBN / 16) + nj * 4 + 2 * tg + (tq >> 1);
+            b[nj][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s16x4_t*)(sb + b16_off(k, c, T::B_ROW) + (tq & 1) * 8));
         }
     };
@@ -247,92 +277,199 @@ __global__ __launch_bounds__((Tile16<TBM, TBN, WN, S>::NT)) void gemm16_kernel(
     // per instruction; at the board's power limit that measured ~0.5 % faster.
     // Each accumulator still sees its k in the same order: the same results.
     auto snake = [](int i) { return ((i / NJ) & 1) ? NJ - 1 - i % NJ : i % NJ; };
-    auto read_frags = [&](int kt, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2]) {
+    // All reads of a pair, in the order the main loop issues them (the
+    // compiler's wait counts at the loop's head are exact only if both paths
+    // into it leave the reads in one order).
+    auto read_frags = [&](int kt, int h, int kp, u32x4 (&a)[MI], s16x4 (&b)[NJ][2]) {
 #pragma unroll
-        for (int i = 0; i < T::NREAD; ++i) read_piece(kt, kp, a, b, i);
+        for (int o = 0; o < T::NREAD; ++o) {
+            read_piece(kt, h, kp, a, b, o);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
-    // Wait until at most VM of this wave's direct-to-LDS loads are in flight and
-    // its LDS accesses are done, then barrier.
-    auto sync = [&](auto vm_tag) {
+    // Wait until at most VM of this wave's direct-to-LDS loads and LGKM of its
+    // LDS accesses are in flight, then barrier.
+    auto sync = [&](auto vm_tag, auto lgkm_tag) {
         constexpr int VM = decltype(vm_tag)::value;
+        constexpr int LGKM = decltype(lgkm_tag)::value;
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, LGKM));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    using OneStepLeft = std::integral_constant<int, (T::S - 1) * T::LOADS>;
-    using TwoStepsLeft = std::integral_constant<int, (T::S - 2) * T::LOADS>;
+    using AllLds = std::integral_constant<int, 0>;
 
-    // Schedule (S stages, KP16 chunk pairs per step), written out in issue
-    // order: with one wave per SIMD nothing else hides a stall, so every
-    // load and LDS read sits between two MFMAs (sched_barrier pins the order).
-    // Prologue: loads of steps 0 .. S - 1.  Step kt: spread over the MFMAs
-    // of pairs 0 and 1, read the fragments of pairs 1 .. KP16 - 1 (one
-    // register set per pair; each pair's reads are issued before its MFMAs
-    // start); then wait until step kt + 1 has landed (later steps may still be
-    // in flight) and barrier, which retires every wave's reads of stage
-    // kt % S; then, spread over the MFMAs of pairs 2 .. KP16 - 1, refill that
-    // stage with step kt + S and read pair 0 of step kt + 1 (its stage landed
-    // before the barrier, and pair 0's registers are free).  Spreading those
-    // reads over both pairs rather than the last one measured 1-4 % faster on
-    // the tiles that are not power-limited.  (A barrier after pair 0, with the
-    // refill over three pairs, measured about 1 % slower.)
-    // The last step reads that pair too (from the stage the empty loads past
-    // K have zero-filled, inside the LDS array; the registers are never
-    // used): an unconditional read saves a branch per matrix instruction.
-    if (nk > 0) {
+    if constexpr (!RINGS) {
+        // SLAB2, written out in issue order (sched_barrier pins it): with one
+        // wave per SIMD nothing else hides a stall, so every load and LDS read
+        // sits between two MFMAs.  Prologue: loads of steps 0 .. S - 1.  Step
+        // kt: spread over the MFMAs of pairs 0 and 1, read the fragments of
+        // pairs 1 .. KP - 1 (one register set per pair; each pair's reads are
+        // issued before its MFMAs start); then wait until step kt + 1 has
+        // landed (later steps may still be in flight) and barrier, which
+        // retires every wave's reads of stage kt % S; then, spread over the
+        // MFMAs of pairs 2 .. KP - 1, refill that stage with step kt + S and
+        // read pair 0 of step kt + 1 (its stage landed before the barrier, and
+        // pair 0's registers are free).  Spreading those reads over both pairs
+        // rather than the last one measured 1-4 % faster on the tiles that are
+        // not power-limited.  (A barrier after pair 0, with the refill over
+        // three pairs, measured about 1 % slower.)  The last step reads that
+        // pair too (from the stage the empty loads past K have zero-filled,
+        // inside the LDS array; the registers are never used): an
+        // unconditional read saves a branch per matrix instruction.
+        using OneStepLeft = std::integral_constant<int, (T::SA - 1) * T::LOADS>;
+        using TwoStepsLeft = std::integral_constant<int, (T::SA - 2) * T::LOADS>;
+        if (nk > 0) {
 #pragma unroll
-        for (int s = 0; s < T::S; ++s) issue_stage(s);
-        sync(OneStepLeft{});
-        if ((K % BK16) && nk == 1) { fix_tail(); sync(OneStepLeft{}); }
-        read_frags(0, 0, fa[0], fb[0]);
-        for (int kt = 0; kt < nk; ++kt) {
-            constexpr int NR = T::NREAD * (KP16 - 1);
+            for (int s = 0; s < T::SA; ++s) {
+                const LoadDesc d = load_desc(s, s);
 #pragma unroll
-            for (int i = 0; i < 2 * T::NMFMA; ++i) {
-                if (i < T::NMFMA) mfma_one(fa[0], fb[0], i / NJ, snake(i));
-                else mfma_one(fa[1], fb[1], (i - T::NMFMA) / NJ, snake(i - T::NMFMA));
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int r = (i * NR) / (2 * T::NMFMA); r < ((i + 1) * NR) / (2 * T::NMFMA); ++r)
-                    read_piece(kt, 1 + r / T::NREAD, fa[1 + r / T::NREAD], fb[1 + r / T::NREAD],
-                               r % T::NREAD);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < T::LOADS; ++j) dma_one(d, 0, j);
             }
-            // Every read of stage kt is now issued: retire them, wait for step
-            // kt + 1, barrier.  The stage is then free for step kt + S.
-            const StageDesc d = stage_desc(kt + T::S);
-            sync(TwoStepsLeft{});
-            if ((K % BK16) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}); }
-            constexpr int SLOTS = T::NMFMA * (KP16 - 2);
+            sync(OneStepLeft{}, AllLds{});
+            if ((K % BKA) && nk == 1) { fix_tail(); sync(OneStepLeft{}, AllLds{}); }
+            read_frags(0, 0, 0, fa[0], fb[0]);
+            for (int kt = 0; kt < nk; ++kt) {
+                constexpr int NR = T::NREAD * (T::KP - 1);
 #pragma unroll
-            for (int kp = 2; kp < KP16; ++kp) {
+                for (int i = 0; i < 2 * T::NMFMA; ++i) {
+                    if (i < T::NMFMA) mfma_one(fa[0], fb[0], i / NJ, snake(i));
+                    else mfma_one(fa[1], fb[1], (i - T::NMFMA) / NJ, snake(i - T::NMFMA));
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = (i * NR) / (2 * T::NMFMA); r < ((i + 1) * NR) / (2 * T::NMFMA); ++r)
+                        read_piece(kt, 0, 1 + r / T::NREAD, fa[1 + r / T::NREAD],
+                                   fb[1 + r / T::NREAD], r % T::NREAD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // Every read of stage kt is now issued: retire them, wait for step
+                // kt + 1, barrier.  The stage is then free for step kt + S.
+                const LoadDesc d = load_desc(kt + T::SA, kt + T::SA);
+                sync(TwoStepsLeft{}, AllLds{});
+                if ((K % BKA) && kt + 2 == nk) { fix_tail(); sync(TwoStepsLeft{}, AllLds{}); }
+                constexpr int SLOTS = T::NMFMA * (T::KP - 2);
+#pragma unroll
+                for (int kp = 2; kp < T::KP; ++kp) {
+#pragma unroll
+                    for (int i = 0; i < T::NMFMA; ++i) {
+                        mfma_one(fa[kp], fb[kp], i / NJ, snake(i));
+                        __builtin_amdgcn_sched_barrier(0);
+                        const int slot = (kp - 2) * T::NMFMA + i;
+#pragma unroll
+                        for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
+                            dma_one(d, 0, j);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int r = (slot * T::NREAD) / SLOTS; r < ((slot + 1) * T::NREAD) / SLOTS; ++r)
+                            read_piece(kt + 1, 0, 0, fa[0], fb[0], r);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+    } else {
+        // RING, written out in issue order like SLAB2.  Loads go out in step
+        // order, LOADS per step (the prologue's first step has no B stage).
+        // Before step 0's first read, A slab 0 and B stage 0 (the prologue's
+        // first two steps) have landed.  At the top of step kt, everything
+        // issued up to step kt - 2 (SA - 2) has landed: B stage kt + 1 was
+        // issued in step kt + 2 - SB, and the slab holding step kt + 1 no later
+        // than that.  LDS accesses complete in order, and the last NREAD a
+        // wave issued before that barrier are its reads of pair 0 of step kt,
+        // from a stage that is not refilled: only the older ones (the previous
+        // step's) must be done before the barrier hands their slots (B stage
+        // (kt - 1) % SB and, when kt is even, A slab ((kt >> 1) - 1) % SA) to
+        // the loads.  Then the two chunk pairs of step kt: pair p's MFMAs carry
+        // the reads of pair p + 1 (of step kt + 1 after the last pair) into the
+        // other register set, in the order of first use, one read per MFMA from
+        // the pair's first slot, so the last of them is several MFMAs old when
+        // the next pair starts; and the step's loads are spread evenly over it.
+        using StepZeroIn = std::integral_constant<int, (2 * T::SA - 4) * T::LOADS>;
+        using NextStepIn = std::integral_constant<int, (2 * T::SA - 5) * T::LOADS>;
+        using NextPairReads = std::integral_constant<int, T::NREAD>;
+        constexpr int RSPAN = T::NREAD <= T::NMFMA ? T::NREAD : T::NMFMA;
+        auto ring_desc = [&](int kt) { return load_desc((kt >> 1) + T::SA - 1, kt + T::SB - 1); };
+        // TAIL: the step at whose top the last A slab has landed
+        // (2 last_slab - 1) zeroes its K tail.  It is peeled off the main loop
+        // so that the loop has no branch, whose join would otherwise make the
+        // compiler wait for every LDS read before the step's first MFMA.
+        auto step = [&](int kt, auto parity_tag, auto tail_tag) {
+            constexpr int H = decltype(parity_tag)::value;     // kt & 1
+            constexpr bool TAIL = decltype(tail_tag)::value;
+            const LoadDesc d = ring_desc(kt);
+            sync(NextStepIn{}, NextPairReads{});
+            if constexpr (TAIL) { fix_tail(); sync(NextStepIn{}, AllLds{}); }
+            constexpr int SLOTS = T::NMFMA * T::KP;
+#pragma unroll
+            for (int kp = 0; kp < T::KP; ++kp) {
 #pragma unroll
                 for (int i = 0; i < T::NMFMA; ++i) {
-                    mfma_one(fa[kp], fb[kp], i / NJ, snake(i));
+                    mfma_one(fa[kp & 1], fb[kp & 1], i / NJ, snake(i));
                     __builtin_amdgcn_sched_barrier(0);
-                    const int slot = (kp - 2) * T::NMFMA + i;
+                    const int slot = kp * T::NMFMA + i;
 #pragma unroll
                     for (int j = (slot * T::LOADS) / SLOTS; j < ((slot + 1) * T::LOADS) / SLOTS; ++j)
-                        dma_one(d, j);
+                        dma_one(d, H, j);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int r = (slot * T::NREAD) / SLOTS; r < ((slot + 1) * T::NREAD) / SLOTS; ++r)
-                        read_piece(kt + 1, 0, fa[0], fb[0], r);
+                    for (int o = (i * T::NREAD) / RSPAN;
+                         o < ((i + 1) * T::NREAD) / RSPAN && o < T::NREAD; ++o) {
+                        if (kp + 1 < T::KP)
+                            read_piece(kt, H, kp + 1, fa[(kp + 1) & 1], fb[(kp + 1) & 1], o);
+                        else
+                            read_piece(kt + 1, 1 - H, 0, fa[0], fb[0], o);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        };
+        using Even = std::integral_constant<int, 0>;
+        using Odd = std::integral_constant<int, 1>;
+        using NoTail = std::false_type;
+        using Tail = std::true_type;
+        if (nk > 0) {
+            for (int kt = -(2 * T::SA - 2); kt < 0; kt += 2) {
+                // Two prologue steps at a time (even, odd).  The first has no B
+                // stage (its index would be -1): only its A loads go out, and
+                // the wait counts only count loads issued after it.
+                const LoadDesc d0 = ring_desc(kt);
+                const int nload = kt + T::SB - 1 >= 0 ? T::LOADS : T::A_DMA;
+                for (int j = 0; j < nload; ++j) dma_one(d0, 0, j);
+                const LoadDesc d1 = ring_desc(kt + 1);
+#pragma unroll
+                for (int j = 0; j < T::LOADS; ++j) dma_one(d1, 1, j);
+            }
+            sync(StepZeroIn{}, AllLds{});
+            // The step that zeroes the last slab's K tail is odd (or -1: before step 0).
+            const int kt_fix = (K % BKA) ? 2 * last_slab - 1 : -2;
+            if (kt_fix == -1) { fix_tail(); sync(StepZeroIn{}, AllLds{}); }
+            read_frags(0, 0, 0, fa[0], fb[0]);
+            int kt = 0;
+            for (; kt + 1 < nk && kt + 1 != kt_fix; kt += 2) {
+                step(kt, Even{}, NoTail{});
+                step(kt + 1, Odd{}, NoTail{});
+            }
+            if (kt + 1 == kt_fix) {
+                step(kt, Even{}, NoTail{});
+                step(kt + 1, Odd{}, Tail{});
+                kt += 2;
+            }
+            for (; kt + 1 < nk; kt += 2) {
+                step(kt, Even{}, NoTail{});
+                step(kt + 1, Odd{}, NoTail{});
+            }
+            if (kt < nk) step(kt, Even{}, NoTail{});
         }
     }
     // No direct-to-LDS write may still be in flight when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-    store_tile<OUT, MI, NJ, EPI>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / WN), g, li,
-                                 epi, m0 + TBM <= M && n0 + TBN <= N);
+    store_tile<OUT, MI, NJ, EPI, PAIRS>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / 2), g, li,
+                                 epi);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI, int WN = 2, int S = 2>
+template <int IN, int OUT, int TBM, int TBN, bool EPI, bool PAIRS, int SCHED, int S>
 hipError_t go(const GemmLaunch& L) {
     const char* a = L.A;
     const char* b = L.B;
@@ -342,24 +479,32 @@ hipError_t go(const GemmLaunch& L) {
     int64_t zs = L.c_zstride;
     EpiArgs e = L.e;
     void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &kchunk, &zs, &e};
-    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI, WN, S>,
-                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits),
-                           dim3(Tile16<TBM, TBN, WN, S>::NT),
+    return hipLaunchKernel((const void*)gemm16_kernel<IN, OUT, TBM, TBN, EPI, PAIRS, SCHED, S>,
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)L.splits), dim3(256),
                            args, 0, L.stream);
 }
 
-template <int IN, int OUT, bool EPI>
+template <int IN, int OUT, bool EPI, bool PAIRS>
 hipError_t by_tile(const GemmLaunch& L) {
-    if (L.tbm == 256 && L.tbn == 256) return go<IN, OUT, 256, 256, EPI>(L);
-    if (L.tbm == 192 && L.tbn == 256) return go<IN, OUT, 192, 256, EPI>(L);
+    if (L.tbm == 256 && L.tbn == 256) return go<IN, OUT, 256, 256, EPI, PAIRS, SLAB2, 2>(L);
+    if (L.tbm == 192 && L.tbn == 256) return go<IN, OUT, 192, 256, EPI, PAIRS, RING, 3>(L);
     if (L.tbm == 128 && L.tbn == 128)
-        return L.stages == 4 ? go<IN, OUT, 128, 128, EPI, 2, 4>(L) : go<IN, OUT, 128, 128, EPI, 2, 2>(L);
+        return L.stages == 4 ? go<IN, OUT, 128, 128, EPI, PAIRS, SLAB2, 4>(L)
+                             : go<IN, OUT, 128, 128, EPI, PAIRS, SLAB2, 2>(L);
     return hipErrorInvalidValue;
+}
+
+// 16-bit C with an even N stores lane pairs; fp32 C, and 16-bit C with an odd
+// N, one element per store.
+template <int IN, int OUT, bool EPI>
+hipError_t by_pairs(const GemmLaunch& L) {
+    if (OUT != OUT_F32 && L.N % 2 == 0) return by_tile<IN, OUT, EPI, true>(L);
+    return by_tile<IN, OUT, EPI, false>(L);
 }
 
 template <int IN, int OUT>
 hipError_t by_epi(const GemmLaunch& L) {
-    return L.epi ? by_tile<IN, OUT, true>(L) : by_tile<IN, OUT, false>(L);
+    return L.epi ? by_pairs<IN, OUT, true>(L) : by_pairs<IN, OUT, false>(L);
 }
 
 }  // namespace

@@ -246,8 +246,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
         }
     }
 
-    store_tile<OUT_F32, MI, MI, EPI>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
-                                     li, epi, m0 + TB <= M && n0 + TB <= N);
+    store_tile<OUT_F32, MI, MI, EPI, false>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
+                                     li, epi);
 }
 
 // ---------------------------------------------------------------- fp32 via 3 x bf16
@@ -623,8 +623,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
         }
     }
 
-    store_tile<OUT_F32, MI, MI, EPI>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
-                                     li, epi, m0 + TB <= M && n0 + TB <= N);
+    store_tile<OUT_F32, MI, MI, EPI, false>(acc, C, M, N, ldc, m0 + wm * (TB / 2), n0 + wn * (TB / 2), g,
+                                     li, epi);
 }
 
 hipError_t go(const void* fn, const GemmLaunch& L) {

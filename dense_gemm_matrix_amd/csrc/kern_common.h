@@ -93,45 +93,63 @@ __device__ __forceinline__ void store_c(char* C, int64_t idx, float v) {
 
 // The fused epilogue on one fp32 sum s: alpha * s + beta * C_old + bias, then
 // the optional ReLU (a NaN passes through), in fp32, before the one rounding
-// to C's format.
+// to C's format.  C_old is the element at byte address p.
 template <int OUT>
-__device__ __forceinline__ float epilogue(float s, const char* C, int64_t idx, float bias,
-                                          const EpiArgs& e) {
+__device__ __forceinline__ float epilogue_at(float s, const char* p, float bias, const EpiArgs& e) {
     float v = e.alpha * s;
-    if (e.beta != 0.0f) v += e.beta * load_c<OUT>(C, idx);
+    if (e.beta != 0.0f) v += e.beta * load_c<OUT>(p, 0);
     v += bias;
     if (e.relu && v < 0.0f) v = 0.0f;
     return v;
 }
 
+// The same for element idx of C.
+template <int OUT>
+__device__ __forceinline__ float epilogue(float s, const char* C, int64_t idx, float bias,
+                                          const EpiArgs& e) {
+    return epilogue_at<OUT>(s, C + idx * (OUT == OUT_F32 ? 4 : 2), bias, e);
+}
+
 // Epilogue of the GEMM kernels.  32x32 accumulator layout: lane (g, li) holds
-// column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4.  Elements
-// outside M x N are not stored; `full` (the whole macro-tile lies inside, a
-// wave-uniform fact) takes a copy of the loop without the per-element tests,
-// which would otherwise become one branch per store.
-template <int OUT, int MI, int NJ, bool EPI, bool FULL>
-__device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
-                                                int ldc, int row0, int col0, int g, int li,
-                                                const EpiArgs& e) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            const int col = col0 + nj * 32 + li;
-            float bias = 0.0f;
-            if (EPI && e.bias && (FULL || col < N)) bias = e.bias[col];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (FULL || (row < M && col < N)) {
-                    const int64_t idx = (int64_t)row * ldc + col;
-                    float v = acc[mi][nj][r];
-                    if constexpr (EPI) v = epilogue<OUT>(v, C, idx, bias, e);
-                    store_c<OUT>(C, idx, v);
-                }
-            }
-        }
-    }
+// column li and, in register r, row 8 * (r / 4) + 4 * g + r % 4 of its block.
+//
+// Every tile takes one branch-free path: a buffer resource over C from the
+// wave's corner (row0, col0) to the end of C's valid region, stores at 32-bit
+// byte offsets = a per-lane part + a wave-uniform part.  Elements past the last
+// row fall outside the resource's range, and lanes whose column is past N get
+// an offset beyond any range (OOB_LANE): the buffer unit drops those stores
+// (and returns zeros for those loads), so nothing outside M x N is written and
+// no element needs a test.  Offsets stay below 2^31 because a 256-row panel of
+// C is under 2 GiB (the ABI's precondition) and a range is at most 2^31 - 16
+// bytes.
+constexpr uint32_t OOB_LANE = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t c_rsrc(char* C, int M, int N, int ldc, int row0,
+                                                         int col0, int es) {
+    char* base = C + ((int64_t)row0 * ldc + col0) * es;
+    int64_t rem = ((int64_t)(M - 1 - row0) * ldc + (N - col0)) * es;
+    if (rem > 0x7ffffff0) rem = 0x7ffffff0;
+    return make_rsrc(base, rem);
+}
+
+template <int OUT>
+__device__ __forceinline__ float load_c_at(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (OUT == OUT_F32)
+        return as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    if constexpr (OUT == OUT_BF16) return as_float(h << 16);
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
+// The fused epilogue on one fp32 sum s read through the C resource.
+template <int OUT>
+__device__ __forceinline__ float epilogue_rs(float s, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                             float bias, const EpiArgs& e) {
+    float v = e.alpha * s;
+    if (e.beta != 0.0f) v += e.beta * load_c_at<OUT>(r, off);
+    v += bias;
+    if (e.relu && v < 0.0f) v = 0.0f;
+    return v;
 }
 
 // Two fp32 values rounded to nearest even in C's 16-bit format, `lo` in the
@@ -155,61 +173,97 @@ __device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_QUAD_XOR1, 0xf, 0xf, false);
 }
 
-// Epilogue for 16-bit C on a tile that lies wholly inside C.  In the 32x32
-// layout an even lane l and lane l + 1 hold columns c and c + 1; registers r
-// and r + 1 (r even) hold rows R and R + 1.  Each lane rounds its two values
-// into one word; one exchange between the two lanes then gives the even lane
-// row R, columns c .. c + 1, and the odd lane row R + 1, the same columns: one
-// 4-byte store where the per-element form needs two 2-byte ones, and each
-// half-wave store writes two 64-byte row pieces instead of one.  The epilogue
-// and the rounding act on each value before the exchange, so the stored values
-// are those of store_tile_impl.  Needs every lane of the wave active.
+// One store per element: fp32 C, or 16-bit C when a tile's column edge falls
+// between the two columns of a lane pair (N odd).
 template <int OUT, int MI, int NJ, bool EPI>
-__device__ __forceinline__ void store_tile16_full(const f32x16 (&acc)[MI][NJ], char* C, int ldc,
-                                                  int row0, int col0, int g, int li,
-                                                  const EpiArgs& e) {
+__device__ __forceinline__ void store_elems(const f32x16 (&acc)[MI][NJ], __amdgpu_buffer_rsrc_t r,
+                                           int N, int ldc, int col0, int g, int li,
+                                           const EpiArgs& e) {
+    constexpr int ES = OUT == OUT_F32 ? 4 : 2;
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int col = col0 + nj * 32 + li;
+        const uint32_t lane = col < N ? (uint32_t)((4 * g * ldc + nj * 32 + li) * ES) : OOB_LANE;
+        float bias = 0.0f;
+        if (EPI && e.bias && col < N) bias = e.bias[col];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const uint32_t off = lane + (uint32_t)((mi * 32 + 8 * (rr >> 2) + (rr & 3)) * ldc * ES);
+                float v = acc[mi][nj][rr];
+                if constexpr (EPI) v = epilogue_rs<OUT>(v, r, off, bias, e);
+                if constexpr (OUT == OUT_F32) {
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+                } else {
+                    const uint32_t p = pack16<OUT>(v, 0.0f);
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)p, r, (int)off, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// 16-bit C with both columns of every lane pair inside or both outside: an
+// even lane l and lane l + 1 hold columns c and c + 1, and registers r and
+// r + 1 (r even) rows R and R + 1.  Each lane rounds its two values into one
+// word; one exchange between the two lanes then gives the even lane row R,
+// columns c .. c + 1, and the odd lane row R + 1, the same columns: one 4-byte
+// store where the per-element form needs two 2-byte ones, and each half-wave
+// store writes two 64-byte row pieces instead of one.  The epilogue and the
+// rounding act on each value before the exchange, so the stored values are
+// those of store_elems.  Needs every lane of the wave active.
+template <int OUT, int MI, int NJ, bool EPI>
+__device__ __forceinline__ void store_pairs16(const f32x16 (&acc)[MI][NJ], __amdgpu_buffer_rsrc_t r,
+                                              int N, int ldc, int col0, int g, int li,
+                                              const EpiArgs& e) {
     const int odd = li & 1;
     // v_perm_b32 takes bytes 0-3 from its second source and 4-7 from its first:
     // the even lane keeps its low half (row R) and takes the neighbour's; the odd
     // lane takes the neighbour's high half (row R + 1) and keeps its own.
     const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int col = col0 + nj * 32 + li;
+        const uint32_t own = col < N ? (uint32_t)((4 * g * ldc + nj * 32 + li) * 2) : OOB_LANE;
+        const uint32_t word = col - odd < N ? (uint32_t)(((4 * g + odd) * ldc + nj * 32 + li - odd) * 2)
+                                            : OOB_LANE;
+        float bias = 0.0f;
+        if (EPI && e.bias && col < N) bias = e.bias[col];
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            const int col = col0 + nj * 32 + li;
-            float bias = 0.0f;
-            if (EPI && e.bias) bias = e.bias[col];
+        for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                float v0 = acc[mi][nj][r];
-                float v1 = acc[mi][nj][r + 1];
+            for (int rr = 0; rr < 16; rr += 2) {
+                const uint32_t rows = (uint32_t)((mi * 32 + 8 * (rr >> 2) + (rr & 3)) * ldc * 2);
+                float v0 = acc[mi][nj][rr];
+                float v1 = acc[mi][nj][rr + 1];
                 if constexpr (EPI) {
-                    v0 = epilogue<OUT>(v0, C, (int64_t)row * ldc + col, bias, e);
-                    v1 = epilogue<OUT>(v1, C, (int64_t)(row + 1) * ldc + col, bias, e);
+                    v0 = epilogue_rs<OUT>(v0, r, own + rows, bias, e);
+                    v1 = epilogue_rs<OUT>(v1, r, own + rows + (uint32_t)(ldc * 2), bias, e);
                 }
                 const uint32_t p = pack16<OUT>(v0, v1);
                 const uint32_t w = __builtin_amdgcn_perm(swap_adjacent_lanes(p), p, sel);
-                const int64_t idx = (int64_t)(row + odd) * ldc + (col - odd);
-                *reinterpret_cast<uint32_t*>(C + idx * 2) = w;
+                __builtin_amdgcn_raw_buffer_store_b32(w, r, (int)(word + rows), 0, 0);
             }
         }
     }
 }
 
-template <int OUT, int MI, int NJ, bool EPI>
+// PAIRS (16-bit C): the launch's N is even, so no lane pair straddles the
+// column edge and every tile takes store_pairs16; with N odd the kernel is
+// instantiated with store_elems instead (deciding inside the kernel costs
+// registers on every tile).
+template <int OUT, int MI, int NJ, bool EPI, bool PAIRS>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[MI][NJ], char* C, int M, int N,
                                            int ldc, int row0, int col0, int g, int li,
-                                           const EpiArgs& e, bool full) {
-    if (full) {
-        if constexpr (OUT == OUT_F32)
-            store_tile_impl<OUT, MI, NJ, EPI, true>(acc, C, M, N, ldc, row0, col0, g, li, e);
-        else
-            store_tile16_full<OUT, MI, NJ, EPI>(acc, C, ldc, row0, col0, g, li, e);
-    } else {
-        store_tile_impl<OUT, MI, NJ, EPI, false>(acc, C, M, N, ldc, row0, col0, g, li, e);
-    }
+                                           const EpiArgs& e) {
+    if (row0 >= M || col0 >= N) return;  // this wave's part of the tile lies outside C
+    constexpr int ES = OUT == OUT_F32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t r = c_rsrc(C, M, N, ldc, row0, col0, ES);
+    if constexpr (OUT != OUT_F32 && PAIRS)
+        store_pairs16<OUT, MI, NJ, EPI>(acc, r, N, ldc, col0, g, li, e);
+    else
+        store_elems<OUT, MI, NJ, EPI>(acc, r, N, ldc, col0, g, li, e);
 }
 
 }  // namespace dgemm

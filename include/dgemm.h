@@ -36,6 +36,9 @@
  *   - A, B and C are 16-byte aligned, and every row pitch in bytes
  *     (lda*esize_in, ldb*esize_in, ldc*esize_out) is a multiple of 16;
  *   - lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N);
+ *   - 256 rows of A, 64 rows of 16-bit B (32 of fp32 B) and 256 rows of C,
+ *     at their row pitches, each span less than 2 GiB (the kernels address
+ *     them with 32-bit buffer offsets): DGEMM_ERR_TOO_LARGE otherwise;
  *   - C's bytes overlap neither A's nor B's.  An operand's bytes are its rows
  *     (row i: row-length elements from base + i * pitch), not the gaps
  *     between them.  Operands with the same row pitch in bytes are compared
@@ -63,7 +66,7 @@ typedef enum {
     DGEMM_ERR_MISALIGNED = 3,    /* a base pointer or a row pitch in bytes not a multiple of 16
                                     (bias: of 4)                                               */
     DGEMM_ERR_ALIAS = 4,         /* C overlaps A, B or the bias; the workspace overlaps any of them */
-    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize or 128*ldb bytes reach 2 GiB (32-bit offsets)  */
+    DGEMM_ERR_TOO_LARGE = 5,     /* 256*lda*esize, 128*ldb or 256*ldc*esize_out bytes reach 2 GiB */
     DGEMM_ERR_DEVICE = 6,        /* no current device, or it is not a gfx950                     */
     DGEMM_ERR_LAUNCH = 7,        /* the kernel launch reported an error                          */
     DGEMM_ERR_SCRATCH_SIZE = 8   /* gemm_ex_static: scratch_bytes > DGEMM_STATIC_SCRATCH_BYTES   */

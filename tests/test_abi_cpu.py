@@ -88,6 +88,9 @@ def test_validation_errors(fn):
     # one K step of B spans 128 * ldb bytes (64 rows of 16-bit data, 32 of fp32)
     far = 0x7000000000
     assert call(fn, 8, 8, 8, PA, ok_ld, PB, (1 << 31) // 128, far, ok_ld) == dg.DGEMM_ERR_TOO_LARGE
+    # a 256-row panel of C spans 256 * ldc * esize_out bytes (fp32 C here)
+    big_c = (1 << 31) // (256 * 4)
+    assert call(fn, 8, 8, 8, PA, ok_ld, PB, ok_ld, far, big_c) == dg.DGEMM_ERR_TOO_LARGE
 
 
 
