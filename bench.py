@@ -6,7 +6,8 @@ the swizzled layout, the matrix-instruction loop and the epilogue all run inside
 that one kernel) on inputs already resident in HBM.  The headline line is the
 bf16 4096^3 product with normal(0,1) inputs and fp32 C; the fp16 (fp16 C) and
 fp32-input 4096^3 products are measured the same way and reported under
-"per_dtype".  Also reported: the same product from a cold cache (each launch
+"per_dtype".  Also reported: the register-only matrix-instruction ceiling the
+bf16 kernel is held to under the board's power limit ("mfma_ceiling"); the same product from a cold cache (each launch
 after a 512 MiB write), with --vendor torch.matmul (hipBLASLt) on the same inputs,
 and the graphics clock and socket power amd-smi reads while the product runs.  The
 other parity workloads, and one GPU's row share of the 4096^3
@@ -17,7 +18,8 @@ bound by the host's launch rate).
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
-                    [--no-power-clock] [--no-cold-cache] [--vendor] [--settle-s S]
+                    [--no-power-clock] [--no-cold-cache] [--no-ceiling] [--vendor]
+                    [--settle-s S]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -118,16 +120,19 @@ def settle_clock(entry, Ad, Bd, Cd, seconds: float) -> int:
     return n
 
 
-def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int, settle_s: float = 0.0):
+def time_gemm(entry, Ad, Bd, Cd, steps: int, warmup: int, settle_s: float = 0.0, info=None):
     """Average kernel duration (s) over `steps` back-to-back launches, timed with
     HIP events recorded on the stream the library launches on, after `warmup`
-    launches and then `settle_s` seconds of launches."""
+    launches and then `settle_s` seconds of launches.  `info` (a dict), if
+    given, receives the number of launches before the timed ones."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         entry(Ad, Bd, Cd, stream=stream)
     torch.cuda.synchronize()
-    settle_clock(entry, Ad, Bd, Cd, settle_s)
+    settled = settle_clock(entry, Ad, Bd, Cd, settle_s)
+    if info is not None:
+        info["launches_before_timed"] = warmup + settled
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -363,6 +368,47 @@ def power_clock(entry, Ad, Bd, Cd, per_launch_s: float, value_tflops: float, pea
                    f"ran {launches} launches back to back"}
 
 
+def mfma_ceiling(gemm_tflops: float, peak: float, steps: int, settle_s: float, with_power: bool):
+    """The register-only matrix-instruction ceiling (libmfma_ceiling.so): one
+    workgroup per CU running the 256 x 256 GEMM kernel's own sequence of
+    v_mfma_f32_32x32x16_bf16 on operands held in registers, drawn from the
+    workload's normal(0,1) bf16 distribution.  Timed like the GEMM, with the
+    clock and power sampled while it runs.  The GEMM's rate over this one is the
+    share of the attainable matrix throughput (at the power limit) that moving
+    the operands leaves."""
+    import ctypes
+    import numpy as np
+    import torch
+    from synth_inputs import draw, to_torch
+    path = os.path.join(ROOT, "dense_gemm_matrix_amd", "libmfma_ceiling.so")
+    lib = ctypes.CDLL(path)
+    lib.mfma_ceiling_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    lib.mfma_ceiling_run.restype = ctypes.c_int
+    grid = int(torch.cuda.get_device_properties(0).multi_processor_count)
+    ops = to_torch(draw(np.random.default_rng(7), (4096 * 8,), "normal", "bf16"), "bf16").to("cuda")
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    iters = 80                       # ~0.1 ms per launch, about one 4096^3 GEMM
+    flop = grid * 4 * iters * 64 * 32768
+
+    def entry(a, b, c, stream=None):
+        st = stream if stream is not None else torch.cuda.current_stream()
+        rc = lib.mfma_ceiling_run(ops.data_ptr(), sink.data_ptr(), iters, grid, st.cuda_stream)
+        if rc:
+            raise RuntimeError(f"mfma_ceiling_run failed ({rc})")
+
+    t, _ = time_gemm(entry, None, None, None, steps, 5, settle_s)
+    ceil_tflops = flop / t / 1e12
+    out = {"tflops": round(ceil_tflops, 2), "frac_of_peak": round(ceil_tflops / peak, 4),
+           "gemm_frac_of_ceiling": round(gemm_tflops / ceil_tflops, 4),
+           "us_per_launch": round(t * 1e6, 2), "launches": steps,
+           "how": f"{grid} workgroups x 4 waves x {iters} x 64 v_mfma_f32_32x32x16_bf16 on "
+                  f"register-resident normal(0,1) bf16 operands, the GEMM kernel's block order"}
+    if with_power:
+        out["power_clock"] = power_clock(entry, None, None, None, t, ceil_tflops, peak)
+    return out
+
+
 def copy_calibration(gib: float = 1.0, reps: int = 5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -459,6 +505,8 @@ def main():
     ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--no-power-clock", action="store_true")
     ap.add_argument("--no-cold-cache", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the register-only matrix-instruction ceiling run")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.matmul (hipBLASLt) on the same inputs, for context")
     ap.add_argument("--settle-s", type=float, default=1.0,
@@ -488,8 +536,9 @@ def main():
     M, N, K = meta["M"], meta["N"], meta["K"]
     torch.cuda.synchronize()
     print(f"bench: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    timing_info = {}
     per_launch, wall = time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, args.warmup,
-                                 args.settle_s)
+                                 args.settle_s, timing_info)
     # Five more timed blocks of the same K steps (no further warm-up), for the
     # spread between trials; `value` stays the first block's.
     trials = [time_gemm(entry[args.dtype], Ad, Bd, Cd, args.steps, 0)[0] for _ in range(5)]
@@ -512,6 +561,7 @@ def main():
         "config": {"workload": DESCRIPTION[name], "M": M, "N": N, "K": K,
                    "frac_of_peak": round(value / peak, 4), "wall_s_timed_region": round(wall, 4),
                    "settle_s": args.settle_s,
+                   "launches_before_timed": timing_info["launches_before_timed"],
                    "trials_ms_per_step": [round(t * 1e3, 5) for t in trials],
                    "trials_median_ms": round(sorted(trials)[2] * 1e3, 5),
                    "trials_min_ms": round(min(trials) * 1e3, 5)},
@@ -541,6 +591,10 @@ def main():
     if not args.no_power_clock:
         print("bench: sampling clock and power under load", file=sys.stderr, flush=True)
         line["power_clock"] = power_clock(entry[args.dtype], Ad, Bd, Cd, per_launch, value, peak)
+    if not args.no_ceiling and args.dtype == "bf16":
+        print("bench: matrix-instruction ceiling", file=sys.stderr, flush=True)
+        line["mfma_ceiling"] = mfma_ceiling(value, peak, args.steps, min(args.settle_s, 1.0),
+                                            not args.no_power_clock)
     if not args.no_per_dtype:
         # The other dtypes of the metric, and fp32 inputs through the 3 x bf16
         # entry (its peak is the bf16 matrix peak: three bf16 products per term).

@@ -12,6 +12,10 @@ CSRC = os.path.join(PKG, "csrc")
 # the C ABI and planner, then one file per kernel family
 SOURCES = [os.path.join(CSRC, f) for f in ("dgemm.hip", "gemm16.hip", "gemm32.hip", "splitk.hip")]
 LIB = os.path.join(PKG, "libdgemm.so")
+# The benchmark's matrix-instruction ceiling kernel: a library of its own,
+# loaded only by bench.py, never by the package.
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libmfma_ceiling.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
@@ -47,6 +51,12 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, CEILING_LIB)
     return LIB
 
 
