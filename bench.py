@@ -477,7 +477,7 @@ def other_shapes(dg, args):
         plan = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(Cd.dtype == Ad.dtype and
                                                                    path != "f32"))
         rec["plan"] = plan
-        if plan["splits"] > 1:
+        if plan["workspace_bytes"] > 0:  # a split-K or Stream-K plan
             ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
 
             def split_entry(a, b, c, stream=None, ws=ws):

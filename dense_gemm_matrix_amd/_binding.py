@@ -44,6 +44,13 @@ _lib.gemm_ex_static.restype = _c_int
 _lib.gemm_ex_plan.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_size_t, _P, _P, _P,
                               ctypes.POINTER(_c_size_t)]
 _lib.gemm_ex_plan.restype = _c_int
+_lib.dgemm_set_plan_override.argtypes = [_c_int, _c_int, _c_int, _c_int]
+_lib.dgemm_set_plan_override.restype = _c_int
+_lib.dgemm_set_stream_k_wait_us.argtypes = [ctypes.c_double]
+_lib.dgemm_set_stream_k_wait_us.restype = _c_int
+_lib.dgemm_stream_k_schedule.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _P,
+                                         _c_int, _P]
+_lib.dgemm_stream_k_schedule.restype = _c_int
 
 DGEMM_OK = 0
 DGEMM_ERR_INVALID_VALUE = 1
@@ -59,6 +66,11 @@ DGEMM_OUT_F32 = 0
 DGEMM_OUT_SAME = 1
 DGEMM_ACT_NONE = 0
 DGEMM_ACT_RELU = 1
+DGEMM_PLAN_AUTO = 0
+DGEMM_PLAN_GRID = 1
+DGEMM_PLAN_STREAM_K = 2
+DGEMM_PLAN_NO_STREAM_K = 3
+SK_ROLES = ("piece", "recompute", "reduce")
 IN_CODES = {"f32": 0, "bf16": 1, "f16": 2, "f32x3": 3}
 _TORCH_IN = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
 
@@ -192,7 +204,42 @@ def gemm_ex_plan(in_fmt: str, M: int, N: int, K: int, workspace_bytes: int,
     _check(_lib.gemm_ex_plan(IN_CODES[in_fmt], out, M, N, K, int(workspace_bytes),
                              *[ctypes.byref(x) for x in v], ctypes.byref(used)))
     return {"tile_rows": v[0].value, "tile_cols": v[1].value, "splits": v[2].value,
-            "workspace_bytes": used.value}
+            "stream_k": v[2].value == 0, "workspace_bytes": used.value}
+
+
+def dgemm_set_plan_override(kind: int, tile_rows: int = 0, tile_cols: int = 0,
+                            splits: int = 1) -> None:
+    """Process-wide plan override of gemm_ex / gemm_ex_static / gemm_ex_plan
+    (DGEMM_PLAN_AUTO clears it); for tests and tuning."""
+    _check(_lib.dgemm_set_plan_override(int(kind), int(tile_rows), int(tile_cols), int(splits)))
+
+
+def dgemm_set_stream_k_wait_us(us: float) -> None:
+    """Longest wait of a Stream-K workgroup for another's partial sums, in
+    microseconds (< 0: the default; 0: never wait, compute missing ones)."""
+    _check(_lib.dgemm_set_stream_k_wait_us(float(us)))
+
+
+def dgemm_stream_k_schedule(in_fmt: str, M: int, N: int, K: int, wg: int,
+                            partials_present: bool = True) -> list:
+    """Host query of the items Stream-K workgroup `wg` runs, in order: a list
+    of dicts (role, tile_m, tile_n, k_begin, k_end, slot, first, last, lo, hi)."""
+    n = ctypes.c_int(0)
+    st = _lib.dgemm_stream_k_schedule(IN_CODES[in_fmt], M, N, K, wg, int(partials_present),
+                                      None, 0, ctypes.byref(n))
+    if n.value == 0:
+        _check(st)
+        return []
+    buf = (ctypes.c_int * (10 * n.value))()
+    _check(_lib.dgemm_stream_k_schedule(IN_CODES[in_fmt], M, N, K, wg, int(partials_present),
+                                        buf, n.value, ctypes.byref(n)))
+    keys = ("role", "tile_m", "tile_n", "k_begin", "k_end", "slot", "first", "last", "lo", "hi")
+    out = []
+    for i in range(n.value):
+        d = dict(zip(keys, buf[10 * i: 10 * i + 10]))
+        d["role"] = SK_ROLES[d["role"]]
+        out.append(d)
+    return out
 
 
 def _ex_args(A, B, C, bias, in_fmt):
@@ -282,7 +329,7 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype=None, *, bias: torch.Tens
         fmt = _TORCH_IN[A.dtype]
         plan = gemm_ex_plan(fmt, A.shape[0], B.shape[1], A.shape[1], 1 << 40,
                             out_same=(out_dtype == A.dtype and fmt != "f32"))
-        if plan["splits"] > 1:
+        if plan["workspace_bytes"] > 0:
             ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=A.device)
     gemm_ex(A, B, C, alpha=alpha, bias=bias, relu=relu, workspace=ws)
     return C

@@ -7,6 +7,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -182,11 +184,14 @@ double step_us(int in) {
     }
 }
 
+enum PlanKind { PLAN_GRID = 0, PLAN_STREAM_K = 1 };
+
 struct Plan {
     int bm, bn;
     int splits, kchunk;   // kchunk: K per split (a multiple of the K step)
     int ldw;              // row pitch of the fp32 partials, in elements
     int64_t ws_bytes;     // workspace the plan uses (0 when unsplit)
+    int kind = PLAN_GRID;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -221,7 +226,72 @@ double estimate_us(int in, int es_out, int M, int N, const TileCand& t, int spli
     return us;
 }
 
-Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail) {
+// ------------------------------------------------------------------ Stream-K
+//
+// The nine-levels tutorial's section 2.9 puts Stream-K beside Split-K: every
+// workgroup gets the same number of K steps, whatever the tile count, so no
+// CU idles.  Here (dgemm_internal.h has the schedule): for grids of at most
+// one 256 x 256 tile per CU, a persistent grid of one workgroup per CU, each
+// computing an equal run of 64-k steps across tile boundaries, then reducing
+// its share of each tile it touched.  Estimated time, fitted to measurements
+// of the kernel (bf16, MI355X, eight shapes from 512 x 4096 x 4096 to
+// 3840 x 3840 x 8192):
+//
+//   SK_FIXED_US + q * step_us * (aligned ? 1 : SK_UNALIGNED)
+//
+// with q = the steps of the longest run.  SK_FIXED_US is mostly the fp32
+// partial tiles' round trip: every workgroup writes at least one 256 KiB
+// tile and its share of the reduction reads as much back, 64-128 MiB in all,
+// more than the XCDs' L2s hold.  When the runs do not start on tile
+// boundaries (a whole number of workgroups per tile), the 32 workgroups of an
+// XCD work at unrelated k offsets of different tiles, and the A and B panels
+// they load are no longer shared through L2 as in the grid plans, where an
+// XCD's tiles advance through k together: each step then costs SK_UNALIGNED
+// times as much.  Stream-K is chosen over the best grid plan (split or not)
+// when predicted SK_MARGIN faster -- on the shapes measured, never -- and
+// never while the stream is being captured into a graph: each launch tags its
+// partials with a fresh 64-bit value from the host, which a replayed graph
+// would repeat.
+
+constexpr double SK_FIXED_US = 33.0;
+constexpr double SK_UNALIGNED = 1.45;
+constexpr double SK_MARGIN = 0.95;
+
+// Whether the Stream-K kernel can run this problem: 16-bit inputs, at least
+// one K step, at most one tile per CU (so no XCD has more tiles than ranks),
+// and at least one iteration per rank on every XCD with a tile (an XCD gets
+// floor or ceil of tiles / 8 of them).
+bool sk_feasible(int in, int M, int N, int K) {
+    if (!(in == IN_BF16 || in == IN_F16) || K <= 0 || M <= 0 || N <= 0) return false;
+    const int64_t nk = ceil_div(K, SK_BK);
+    const int64_t tiles = ceil_div(M, SK_TILE) * ceil_div(N, SK_TILE);
+    const int64_t nx_min = std::max<int64_t>(1, tiles / NUM_XCD);
+    return tiles <= NUM_CU && nk < ((int64_t)1 << 24) && nx_min * nk >= NUM_CU / NUM_XCD;
+}
+
+double estimate_sk_us(int in, int M, int N, int K) {
+    const int64_t nk = ceil_div(K, SK_BK);
+    const int64_t tiles = ceil_div(M, SK_TILE) * ceil_div(N, SK_TILE);
+    const int64_t R = NUM_CU / NUM_XCD;
+    const int64_t nx = ceil_div(tiles, NUM_XCD);
+    const bool aligned = tiles % NUM_XCD == 0 && R % nx == 0;
+    const double q = (double)ceil_div(nx * nk, R);
+    return SK_FIXED_US + q * step_us(in) * (aligned ? 1.0 : SK_UNALIGNED);
+}
+
+Plan sk_plan(int M, int N, int K) {
+    Plan p{SK_TILE, SK_TILE, 1, K, 0, sk_ws_bytes(NUM_CU)};
+    p.kind = PLAN_STREAM_K;
+    (void)M;
+    (void)N;
+    return p;
+}
+
+// Plan choice forced by dgemm_set_plan_override (tests and tuning).
+std::atomic<int> g_override_kind{DGEMM_PLAN_AUTO};
+std::atomic<int> g_override_bm{0}, g_override_bn{0}, g_override_splits{1};
+
+Plan make_plan_auto(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool allow_sk) {
     const TileCand base = pick_tile(in, M, N);
     Plan plan{base.bm, base.bn, 1, K, 0, 0};
     if (ws_avail == 0 || K == 0 || M == 0 || N == 0) return plan;
@@ -247,7 +317,77 @@ Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail) {
             }
         }
     }
+    if (allow_sk && sk_feasible(in, M, N, K) && (uint64_t)sk_ws_bytes(NUM_CU) <= ws_avail &&
+        estimate_sk_us(in, M, N, K) < best * SK_MARGIN)
+        plan = sk_plan(M, N, K);
     return plan;
+}
+
+// The plan of a call: the override when one is set and this call can take
+// it, else the estimate's choice.
+Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool allow_sk) {
+    const int kind = g_override_kind.load(std::memory_order_relaxed);
+    if (kind == DGEMM_PLAN_STREAM_K && allow_sk && sk_feasible(in, M, N, K) &&
+        (uint64_t)sk_ws_bytes(NUM_CU) <= ws_avail)
+        return sk_plan(M, N, K);
+    if (kind == DGEMM_PLAN_GRID && M > 0 && N > 0) {
+        const int bm = g_override_bm.load(std::memory_order_relaxed);
+        const int bn = g_override_bn.load(std::memory_order_relaxed);
+        int n = 0;
+        const TileCand* cands = tiles_for(in, n);
+        for (int c = 0; c < n; ++c) {
+            if (cands[c].bm != bm || cands[c].bn != bn) continue;
+            const int bk = bk_of(in);
+            const int nk = (int)std::max<int64_t>(ceil_div(K, bk), 1);
+            const int s = std::min(g_override_splits.load(std::memory_order_relaxed), nk);
+            const int steps = (int)ceil_div(nk, s);
+            const int splits = (int)ceil_div(nk, steps);
+            const int ldw = (int)ceil_div(N, 4) * 4;
+            const int64_t ws = splits > 1 ? (int64_t)splits * M * ldw * 4 : 0;
+            if (splits > 1 && ((uint64_t)ws > ws_avail || K == 0 ||
+                               (int64_t)PANEL_ROWS * ldw * 4 >= DESC_LIMIT ||
+                               ceil_div(M, bm) * ceil_div(N, bn) * splits > INT32_MAX))
+                break;
+            return splits > 1 ? Plan{bm, bn, splits, steps * bk, ldw, ws} : Plan{bm, bn, 1, K, 0, 0};
+        }
+    }
+    return make_plan_auto(in, es_out, M, N, K, ws_avail, allow_sk && kind != DGEMM_PLAN_NO_STREAM_K);
+}
+
+// Stream-K launches tag their partials with a value no earlier launch used:
+// a process-wide counter from a start drawn from the clock and an address, so
+// that flags another process left in a reused buffer are not taken either.
+std::atomic<unsigned long long> g_sk_epoch{
+    ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() *
+     0x9E3779B97F4A7C15ull) ^ (unsigned long long)(uintptr_t)&g_override_kind};
+
+std::atomic<double> g_sk_wait_us{-1.0};  // < 0: from the estimate
+std::atomic<int> g_wall_khz[256];        // wall-clock rate per device (0: not yet read)
+
+// Longest wait of an owner for one partial, in wall-clock ticks: by default
+// twice the estimated kernel time plus 100 us (a partial is normally long
+// done by then; only a grid that is not co-resident misses it, and the owner
+// then computes it itself).
+long long sk_wait_ticks(double est_us) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) dev = 0;
+    int khz = g_wall_khz[dev].load(std::memory_order_relaxed);
+    if (khz <= 0) {
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz <= 0)
+            khz = 100000;  // 100 MHz, the MI300-series constant clock
+        g_wall_khz[dev].store(khz, std::memory_order_relaxed);
+    }
+    double us = g_sk_wait_us.load(std::memory_order_relaxed);
+    if (us < 0.0) us = 2.0 * est_us + 100.0;
+    return (long long)(us * khz / 1000.0);
+}
+
+// Whether `stream` is being captured into a graph (or the query fails).
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return true;
+    return st != hipStreamCaptureStatusNone;
 }
 
 bool epi_needed(const EpiArgs& e) {
@@ -258,11 +398,10 @@ hipError_t launch_family(const GemmLaunch& L) {
     return (L.in == IN_BF16 || L.in == IN_F16) ? launch_gemm16(L) : launch_gemm32(L);
 }
 
-// Validated arguments -> one GEMM launch, or a split GEMM into the workspace
-// followed by the reduction.
+// Validated arguments and a plan -> one GEMM launch, a split GEMM into the
+// workspace followed by the reduction, or a Stream-K launch.
 int run(int in, int outfmt, int M, int N, int K, const void* A, int lda, const void* B, int ldb,
-        void* C, int ldc, const EpiArgs& e, void* ws, uint64_t ws_bytes, hipStream_t stream) {
-    const Plan p = make_plan(in, out_esize(outfmt), M, N, K, ws ? ws_bytes : 0);
+        void* C, int ldc, const EpiArgs& e, const Plan& p, void* ws, hipStream_t stream) {
     GemmLaunch L{};
     L.in = in;
     L.tbm = p.bm;
@@ -284,6 +423,24 @@ int run(int in, int outfmt, int M, int N, int K, const void* A, int lda, const v
     // issued three steps ahead) measured 17-27 % faster.
     const int64_t wgs = (int64_t)L.tiles_m * L.tiles_n * p.splits;
     L.stages = (p.bm == 128 && (in == IN_BF16 || in == IN_F16) && wgs <= NUM_CU) ? 4 : 2;
+    if (p.kind == PLAN_STREAM_K) {
+        L.out = outfmt;
+        L.epi = epi_needed(e);
+        L.C = (char*)C;
+        L.ldc = ldc;
+        L.splits = 1;
+        L.kchunk = K;
+        L.e = e;
+        SkSched s{};
+        s.tiles_m = L.tiles_m;
+        s.tiles_n = L.tiles_n;
+        s.nk = (int)ceil_div(K, SK_BK);
+        s.part = (char*)ws;
+        s.flags = (unsigned long long*)((char*)ws + sk_ws_bytes(NUM_CU) - (int64_t)NUM_CU * 8);
+        s.epoch = g_sk_epoch.fetch_add(1, std::memory_order_relaxed);
+        s.wait_ticks = sk_wait_ticks(estimate_sk_us(in, M, N, K));
+        return launch_gemm16_sk(L, s, NUM_CU) == hipSuccess ? DGEMM_OK : DGEMM_ERR_LAUNCH;
+    }
     if (p.splits == 1) {
         L.out = outfmt;
         L.epi = epi_needed(e);
@@ -327,7 +484,8 @@ int gemm_plain(int in, int M, int N, int K, const void* A, int lda, const void* 
     if (M == 0 || N == 0) return DGEMM_OK;
     st = check_device();
     if (st != DGEMM_OK) return st;
-    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{1.0f, 0.0f, nullptr, 0}, nullptr, 0,
+    const Plan p = make_plan_auto(in, out_esize(of), M, N, K, 0, false);
+    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{1.0f, 0.0f, nullptr, 0}, p, nullptr,
                (hipStream_t)stream);
 }
 
@@ -379,8 +537,10 @@ int gemm_ex_impl(int in, int out, int M, int N, int K, const void* A, int lda, c
     const Span c = matrix_span(C, M, N, ldc, es_out);
     const Span b = matrix_span(bias, 1, N, N, 4);
     if (bias && spans_overlap(c, b)) return DGEMM_ERR_ALIAS;
-    const Plan p = make_plan(in, es_out, M, N, K, (use_static || workspace) ? workspace_bytes : 0);
-    if (p.splits > 1 && !use_static) {
+    const bool allow_sk = !capturing((hipStream_t)stream);
+    const Plan p =
+        make_plan(in, es_out, M, N, K, (use_static || workspace) ? workspace_bytes : 0, allow_sk);
+    if (p.ws_bytes > 0 && !use_static) {
         const int es = in_esize(in);
         const Span w = matrix_span(workspace, 1, p.ws_bytes, p.ws_bytes, 1);
         if (spans_overlap(w, c) || spans_overlap(w, matrix_span(A, M, K, lda, es)) ||
@@ -390,7 +550,7 @@ int gemm_ex_impl(int in, int out, int M, int N, int K, const void* A, int lda, c
     st = check_device();
     if (st != DGEMM_OK) return st;
     if (use_static) {
-        if (p.splits > 1) {
+        if (p.ws_bytes > 0) {
             st = static_scratch(&workspace);
             if (st != DGEMM_OK) return st;
         } else {
@@ -398,8 +558,8 @@ int gemm_ex_impl(int in, int out, int M, int N, int K, const void* A, int lda, c
             workspace_bytes = 0;
         }
     }
-    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{alpha, beta, bias, act}, workspace,
-               workspace_bytes, (hipStream_t)stream);
+    return run(in, of, M, N, K, A, lda, B, ldb, C, ldc, EpiArgs{alpha, beta, bias, act}, p, workspace,
+               (hipStream_t)stream);
 }
 
 }  // namespace
@@ -450,12 +610,83 @@ int gemm_ex_plan(int in, int out, int M, int N, int K, size_t workspace_bytes, i
     const int of = out_format(in, out);
     if (of < 0) return DGEMM_ERR_INVALID_VALUE;
     if (ceil_div(M, 128) * ceil_div(N, 128) > INT32_MAX) return DGEMM_ERR_TOO_LARGE;
-    const Plan p = make_plan(in, out_esize(of), M, N, K, workspace_bytes);
+    const Plan p = make_plan(in, out_esize(of), M, N, K, workspace_bytes, true);
     if (tile_rows) *tile_rows = p.bm;
     if (tile_cols) *tile_cols = p.bn;
-    if (splits) *splits = p.splits;
+    if (splits) *splits = p.kind == PLAN_STREAM_K ? 0 : p.splits;
     if (workspace_used) *workspace_used = (size_t)p.ws_bytes;
     return DGEMM_OK;
+}
+
+int dgemm_set_plan_override(int kind, int tile_rows, int tile_cols, int splits) {
+    if (kind != DGEMM_PLAN_AUTO && kind != DGEMM_PLAN_GRID && kind != DGEMM_PLAN_STREAM_K &&
+        kind != DGEMM_PLAN_NO_STREAM_K)
+        return DGEMM_ERR_INVALID_VALUE;
+    if (kind == DGEMM_PLAN_GRID && splits < 1) return DGEMM_ERR_INVALID_VALUE;
+    g_override_bm.store(tile_rows, std::memory_order_relaxed);
+    g_override_bn.store(tile_cols, std::memory_order_relaxed);
+    g_override_splits.store(kind == DGEMM_PLAN_GRID ? splits : 1, std::memory_order_relaxed);
+    g_override_kind.store(kind, std::memory_order_relaxed);
+    return DGEMM_OK;
+}
+
+int dgemm_set_stream_k_wait_us(double us) {
+    if (std::isnan(us)) return DGEMM_ERR_INVALID_VALUE;
+    g_sk_wait_us.store(us < 0.0 ? -1.0 : us, std::memory_order_relaxed);
+    return DGEMM_OK;
+}
+
+int dgemm_stream_k_schedule(int in, int M, int N, int K, int wg, int partials_present, int* items,
+                            int max_items, int* n_items) {
+    if (n_items) *n_items = 0;
+    if (M < 0 || N < 0 || K < 0 || max_items < 0 || (max_items > 0 && !items)) return DGEMM_ERR_INVALID_VALUE;
+    if (in != DGEMM_IN_BF16 && in != DGEMM_IN_F16) return DGEMM_ERR_INVALID_VALUE;
+    if (!sk_feasible(in, M, N, K) || wg < 0 || wg >= NUM_CU) return DGEMM_ERR_INVALID_VALUE;
+    const int G = NUM_CU;
+    SkSched sk{};
+    sk.tiles_m = (int)ceil_div(M, SK_TILE);
+    sk.tiles_n = (int)ceil_div(N, SK_TILE);
+    sk.nk = (int)ceil_div(K, SK_BK);
+    const SkRun r = sk_run(sk, wg, G);
+    int n = 0;
+    auto put = [&](int role, int u, int kb, int ke, int slot, int lo, int hi) {
+        if (n < max_items) {
+            int tm, tn;
+            map_tile(r.pos(u), sk.tiles_m, sk.tiles_n, tm, tn);
+            int* o = items + 10 * n;
+            o[0] = role;
+            o[1] = tm;
+            o[2] = tn;
+            o[3] = kb * SK_BK;
+            o[4] = ke == sk.nk ? K : ke * SK_BK;
+            o[5] = slot;
+            o[6] = r.first(u);
+            o[7] = r.last(u);
+            o[8] = lo;
+            o[9] = hi;
+        }
+        ++n;
+    };
+    // The kernel's order, with every other contributor's piece published or
+    // every one missing.
+    int kb, ke, lo, hi;
+    for (int pc = 0; pc < r.npieces; ++pc) {
+        r.piece(r.j, r.u0 + pc, kb, ke);
+        put(DGEMM_SK_PIECE, r.u0 + pc, kb, ke, r.slot(r.j, r.u0 + pc), 0, 0);
+    }
+    for (int pc = 0; pc < r.npieces; ++pc) {
+        const int u = r.u0 + pc;
+        if (!partials_present)
+            for (int p = r.first(u); p <= r.last(u); ++p) {
+                if (p == r.j) continue;
+                r.piece(p, u, kb, ke);
+                put(DGEMM_SK_RECOMPUTE, u, kb, ke, r.slot(p, u), 0, 0);
+            }
+        sk_share(r, u, lo, hi);
+        put(DGEMM_SK_REDUCE, u, 0, 0, -1, lo, hi);
+    }
+    if (n_items) *n_items = n;
+    return n <= max_items ? DGEMM_OK : DGEMM_ERR_INVALID_VALUE;
 }
 
 const char* dgemm_status_string(int status) {

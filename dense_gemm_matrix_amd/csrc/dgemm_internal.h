@@ -69,9 +69,117 @@ struct GemmLaunch {
     hipStream_t stream;
 };
 
+// ------------------------------------------------------------------ Stream-K
+//
+// The nine-levels tutorial's section 2.9 names Stream-K as the refinement of
+// Split-K that gives every thread block the same amount of work.  Here, for
+// grids of at most one 256 x 256 tile per CU (the 16-bit kernel's tile), a
+// persistent grid of G workgroups (G a multiple of the 8 XCDs, one per CU):
+// the tiles map_tile gives XCD x (tile walk positions x + 8 u, u < n_x) are
+// laid end to end as W = n_x nk iterations (one iteration = one 64-k step of
+// one tile), and XCD x's R = G / 8 workgroups (b = x + 8 j, rank j) take
+// consecutive runs of equal length: rank j covers [floor(j W / R),
+// floor((j + 1) W / R)).  The host keeps n_x <= R (so a run is at most nk
+// iterations long and touches at most two tiles) and W >= R (so no run is
+// empty).
+//
+// A rank computes the pieces of its run (one or two: the k range it holds of
+// each tile it touches) into fp32 partial-tile slots, then publishes them with
+// one flag.  Each tile is then reduced by all of its contributors together:
+// the tile's 64 blocks of 32 x 32 outputs are dealt out in equal runs, and the
+// i-th of its n contributors sums its blocks' partials in contributor order
+// (k order), applies the epilogue and stores them.  Every output is so added
+// in one fixed order whatever the timing: a deterministic fix-up with no
+// atomic arithmetic, whose reads are shared evenly by the workgroups of the
+// tile.  All contributors of a tile are on one XCD, so partial sums meet in
+// that XCD's L2.
+//
+// Waits are bounded: a reducer waits for a contributor's flag at most
+// wait_ticks (wall-clock ticks); a piece that has not appeared by then (its
+// rank has not started, for instance because the grid is not co-resident) the
+// reducer computes itself, into that rank's slot, with the same code on the
+// same data: the bits the contributor writes, so a late contributor
+// overwrites them with themselves.  No wait can therefore hang the kernel, and
+// the output never depends on which path ran.  A flag holds the launch's
+// 64-bit epoch (a new value per launch from the host), so flags left by
+// earlier launches in the workspace are never taken for this launch's.
+//
+// part: 2 G fp32 tiles of 256 KiB (slots 2 b and 2 b + 1: workgroup b's first
+// and second piece); flags: G 64-bit words.
+struct SkSched {
+    int tiles_m, tiles_n;
+    int nk;         // 64-k steps per tile
+    char* part;
+    unsigned long long* flags;
+    unsigned long long epoch;
+    long long wait_ticks;
+};
+
+constexpr int SK_TILE = 256;    // the Stream-K macro-tile, square
+constexpr int SK_BK = 64;       // k per iteration
+constexpr int SK_BLOCKS = 64;   // 32 x 32 output blocks per tile
+
+// Rank j of XCD x and its run [s0, s1) of the XCD's W iterations.
+struct SkRun {
+    int x, j, R, nk, W, s0, s1;
+    int u0;        // the tile of the first piece (of the XCD's list)
+    int npieces;   // 1 or 2 (the second: tile u0 + 1)
+    __host__ __device__ int start(int r) const { return (int)((int64_t)r * W / R); }
+    __host__ __device__ int pos(int u) const { return x + NUM_XCD * u; }  // tile walk position
+    __host__ __device__ int rank_of(int it) const {  // the rank whose run holds iteration it
+        return (int)((((int64_t)it + 1) * R - 1) / W);
+    }
+    __host__ __device__ int first(int u) const { return rank_of(u * nk); }
+    __host__ __device__ int last(int u) const { return rank_of((u + 1) * nk - 1); }
+    // Slot of rank p's piece of tile u.
+    __host__ __device__ int slot(int p, int u) const {
+        return 2 * (x + NUM_XCD * p) + (start(p) / nk == u ? 0 : 1);
+    }
+    // Rank p's k range [kb, ke) of tile u, in iterations of the tile.
+    __host__ __device__ void piece(int p, int u, int& kb, int& ke) const {
+        const int t0 = u * nk;
+        const int a = start(p), b = start(p + 1);
+        kb = (a > t0 ? a : t0) - t0;
+        ke = (b < t0 + nk ? b : t0 + nk) - t0;
+    }
+};
+
+__host__ __device__ inline SkRun sk_run(const SkSched& sk, int b, int G) {
+    SkRun r;
+    r.x = b % NUM_XCD;
+    r.j = b / NUM_XCD;
+    r.R = G / NUM_XCD;
+    r.nk = sk.nk;
+    const int tiles = sk.tiles_m * sk.tiles_n;
+    const int nx = tiles > r.x ? (tiles - r.x + NUM_XCD - 1) / NUM_XCD : 0;
+    r.W = nx * sk.nk;
+    r.s0 = r.start(r.j);
+    r.s1 = r.start(r.j + 1);
+    r.u0 = r.W > 0 ? r.s0 / sk.nk : 0;
+    r.npieces = r.W == 0 ? 0 : (r.s1 > (r.u0 + 1) * sk.nk ? 2 : 1);
+    return r;
+}
+
+// Blocks [lo, hi) of tile u that rank j reduces: its share among the tile's
+// contributors first(u) .. last(u).
+__host__ __device__ inline void sk_share(const SkRun& r, int u, int& lo, int& hi) {
+    const int f = r.first(u), n = r.last(u) - f + 1, i = r.j - f;
+    lo = SK_BLOCKS * i / n;
+    hi = SK_BLOCKS * (i + 1) / n;
+}
+
+// Workspace of a Stream-K launch of `grid` workgroups: 2 grid partial tiles,
+// then one 64-bit flag per workgroup.
+constexpr int64_t sk_ws_bytes(int grid) {
+    return (int64_t)2 * grid * SK_TILE * SK_TILE * 4 + (int64_t)grid * 8;
+}
+
 // Per kernel family; each returns hipErrorInvalidValue for a combination it
 // has no instantiation for.
 hipError_t launch_gemm16(const GemmLaunch& L);  // IN_BF16, IN_F16
+// The Stream-K launch: L as for launch_gemm16 with tbm = tbn = 256 and
+// splits = 1; `grid` workgroups, a multiple of NUM_XCD.
+hipError_t launch_gemm16_sk(const GemmLaunch& L, const SkSched& s, int grid);
 hipError_t launch_gemm32(const GemmLaunch& L);  // IN_F32, IN_F32X3
 
 // Split-K reduction: C[i][j] = epilogue(sum_{z < splits} W[z][i][j]) with W

@@ -108,37 +108,30 @@ __device__ __forceinline__ int b16_off(int k, int chunk, int row_bytes) {
     return k * row_bytes + ((chunk ^ b16_swz(k)) << 4);
 }
 
-template <int IN, int OUT, int TBM, int TBN, bool EPI, bool PAIRS, int SCHED, int S>
-__global__ __launch_bounds__(256) void gemm16_kernel(
-    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
-    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
-    int kchunk, int64_t c_zstride, EpiArgs epi) {
+// The K loop of one macro-tile: acc := A[m0 .. m0 + TBM) x B[.., n0 .. n0 + TBN)
+// over k in [0, K), with A and B already offset to the first k and rows_a /
+// cols_b the tile's rows of A and columns of B inside the matrices (ZERO =
+// false: acc += that product, the matrix instructions accumulating onto acc's
+// values).  smem is the workgroup's LDS ring (Tile16::LDS bytes).  Every wave
+// of the workgroup calls it together; on return no load or LDS access of this
+// wave is in flight, but other waves may still be reading the ring.
+template <int IN, int TBM, int TBN, int SCHED, int S, bool ZERO = true, bool PER_CALL = false>
+__device__ __forceinline__ void mainloop16(const char* __restrict__ A, const char* __restrict__ B,
+                                           int K, int lda, int ldb, int m0, int n0, int rows_a,
+                                           int cols_b, char* smem,
+                                           f32x16 (&acc)[TBM / 64][TBN / 64]) {
     using T = Tile16<TBM, TBN, SCHED, S>;
     constexpr bool RINGS = T::R;
-    // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
-    // and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when unsplit).
-    {
-        const int z = (int)blockIdx.y;
-        const int kbeg = z * kchunk;
-        A += (int64_t)kbeg * 2;
-        B += (int64_t)kbeg * ldb * 2;
-        C += z * c_zstride;
-        K = (K - kbeg) < kchunk ? (K - kbeg) : kchunk;
-    }
     constexpr int MI = T::MI, NJ = T::NJ;
-    __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
     char* const smA = smem;
     char* const smB = smem + T::SA * T::A_STAGE;
-
-    int tm, tn;
-    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int tid = (int)threadIdx.x;
+    int tid = (int)threadIdx.x;
+    // PER_CALL (a caller that runs several K loops): make the lane's offsets
+    // opaque per call, so the compiler derives them inside each call rather
+    // than keeping them in registers across the caller's loop.
+    if constexpr (PER_CALL) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-    const int m0 = tm * TBM;
-    const int n0 = tn * TBN;
-    const int rows_a = (M - m0) < TBM ? (M - m0) : TBM;
-    const int cols_b = (N - n0) < TBN ? (N - n0) : TBN;
     const int nk = (K + T::STEPK - 1) / T::STEPK;   // loop steps
 
     // Each direct-to-LDS instruction fills a 1 KiB block lane-linearly (lane l
@@ -225,13 +218,14 @@ __global__ __launch_bounds__(256) void gemm16_kernel(
     const int tq = lane & 3;          // transpose read: source 4-column piece
     const int tg = (lane >> 4) & 1;   // transpose read: the 16-lane group's column half
 
-    f32x16 acc[MI][NJ];
+    if constexpr (ZERO) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
+            for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+    }
 
     // Operand fragments, one register set per chunk pair of a step (SLAB2) or
     // two sets that the pairs alternate between (RING): A as MI x 8
@@ -464,9 +458,261 @@ __global__ __launch_bounds__(256) void gemm16_kernel(
     }
     // No direct-to-LDS write may still be in flight when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+}
 
-    store_tile<OUT, MI, NJ, EPI, PAIRS>(acc, C, M, N, ldc, m0 + wm * (TBM / 2), n0 + wn * (TBN / 2), g, li,
-                                 epi);
+// One macro-tile per workgroup: tile map_tile(blockIdx.x), k range blockIdx.y.
+template <int IN, int OUT, int TBM, int TBN, bool EPI, bool PAIRS, int SCHED, int S>
+__global__ __launch_bounds__(256) void gemm16_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n,
+    int kchunk, int64_t c_zstride, EpiArgs epi) {
+    using T = Tile16<TBM, TBN, SCHED, S>;
+    // Split-K: workgroup row z of the grid covers k in [z kchunk, (z+1) kchunk)
+    // and writes its partial sums at C + z c_zstride (z = 0, kchunk = K when unsplit).
+    {
+        const int z = (int)blockIdx.y;
+        const int kbeg = z * kchunk;
+        A += (int64_t)kbeg * 2;
+        B += (int64_t)kbeg * ldb * 2;
+        C += z * c_zstride;
+        K = (K - kbeg) < kchunk ? (K - kbeg) : kchunk;
+    }
+    __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * TBM;
+    const int n0 = tn * TBN;
+    const int rows_a = (M - m0) < TBM ? (M - m0) : TBM;
+    const int cols_b = (N - n0) < TBN ? (N - n0) : TBN;
+    f32x16 acc[T::MI][T::NJ];
+    mainloop16<IN, TBM, TBN, SCHED, S>(A, B, K, lda, ldb, m0, n0, rows_a, cols_b, smem, acc);
+    const int lane = (int)threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    store_tile<OUT, T::MI, T::NJ, EPI, PAIRS>(acc, C, M, N, ldc, m0 + (wave >> 1) * (TBM / 2),
+                                              n0 + (wave & 1) * (TBN / 2), lane >> 5, lane & 31, epi);
+}
+
+// ------------------------------------------------------------------ Stream-K
+//
+// The schedule (which workgroup computes which k range of which tile, and
+// which blocks of each tile it reduces) is in dgemm_internal.h, shared with
+// the host-side query of it.  This kernel runs it: one persistent workgroup
+// per CU, the 256 x 256 SLAB2 K loop for every piece.
+
+using SkTile = Tile16<SK_TILE, SK_TILE, SLAB2, 2>;
+constexpr int SK_SLOT = SK_TILE * SK_TILE * 4;  // bytes of one fp32 partial tile
+
+// A partial tile in the accumulators' own layout: lane l of wave w keeps
+// acc[mi][nj][4 c .. 4 c + 3] in 16-byte piece ((w MI NJ + mi NJ + nj) 4 + c) 64 + l
+// of the slot, so every store and load instruction moves one contiguous KiB,
+// and 32 x 32 output block q = w MI NJ + mi NJ + nj is the slot's KiB pieces
+// 4 q .. 4 q + 3.
+template <int MI, int NJ>
+__device__ __forceinline__ void part_store(const f32x16 (&acc)[MI][NJ], char* slot, int wave,
+                                           int lane) {
+    f32x4* p = (f32x4*)slot + wave * (MI * NJ * 4 * 64) + lane;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                p[((mi * NJ + nj) * 4 + c) * 64] =
+                    f32x4{acc[mi][nj][4 * c], acc[mi][nj][4 * c + 1], acc[mi][nj][4 * c + 2],
+                          acc[mi][nj][4 * c + 3]};
+}
+
+// This workgroup's share of tile u's reduction: blocks [lo, hi) of the tile,
+// dealt to the four waves in turn.  Each output is the sum of the partials of
+// the tile's contributors first .. last, added in that order, then the
+// epilogue and the one-tile kernel's store of a 32 x 32 block (the
+// accumulator layout the slot keeps).  Loads go out SK_BATCH contributors at
+// a time, ahead of their additions.  Every partial is in its slot and visible
+// to this workgroup.
+constexpr int SK_BATCH = 8;
+
+// A function of its own (arguments in registers), so that its registers are
+// allocated apart from the K loop's.
+template <int OUT, bool EPI, bool PAIRS>
+__device__ __attribute__((noinline)) void sk_reduce(int x, int j, int W, int nk, int u, int tm,
+                                                    int tn, const char* part, char* C, int M,
+                                                    int N, int ldc, int wave, int lane,
+                                                    float alpha, float beta, const float* bias,
+                                                    int relu) {
+    constexpr int MI = SkTile::MI, NJ = SkTile::NJ;
+    SkRun r{};
+    r.x = x;
+    r.j = j;
+    r.R = (int)gridDim.x / NUM_XCD;
+    r.W = W;
+    r.nk = nk;
+    const EpiArgs e{alpha, beta, bias, relu};
+    int lo, hi;
+    sk_share(r, u, lo, hi);
+    const int f = r.first(u), l = r.last(u);
+    for (int q = lo + wave; q < hi; q += 4) {
+        f32x4 s[4];
+        for (int p0 = f; p0 <= l; p0 += SK_BATCH) {
+            f32x4 v[SK_BATCH][4];
+#pragma unroll
+            for (int i = 0; i < SK_BATCH; ++i) {
+                if (p0 + i > l) break;  // wave-uniform
+                const f32x4* src =
+                    (const f32x4*)(part + (int64_t)r.slot(p0 + i, u) * SK_SLOT) + q * 256 + lane;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[i][c] = src[c * 64];
+            }
+#pragma unroll
+            for (int i = 0; i < SK_BATCH; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (p0 + i == f) s[c] = v[i][c];
+                    else if (p0 + i <= l) s[c] += v[i][c];
+                }
+        }
+        f32x16 t[1][1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t[0][0][4 * c + k] = s[c][k];
+        const int w = q / (MI * NJ), mi = (q / NJ) % MI, nj = q % NJ;
+        store_tile<OUT, 1, 1, EPI, PAIRS>(t, C, M, N, ldc,
+                                          tm * SK_TILE + (w >> 1) * (SK_TILE / 2) + mi * 32,
+                                          tn * SK_TILE + (w & 1) * (SK_TILE / 2) + nj * 32,
+                                          lane >> 5, lane & 31, e);
+    }
+}
+
+template <int IN, int OUT, bool EPI, bool PAIRS>
+__global__ __launch_bounds__(256) void gemm16_sk_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C, int M, int N,
+    int K, int lda, int ldb, int ldc, SkSched sk, EpiArgs epi) {
+    using T = SkTile;
+    constexpr int MI = T::MI, NJ = T::NJ;
+    __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+    __shared__ int s_missing;
+    const int G = (int)gridDim.x;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // The first rank in [p, hi] other than `self` whose flag does not hold
+    // this launch's epoch within wait_ticks (hi + 1 if none), polled by one
+    // thread with plain atomic loads; one acquire then makes every published
+    // piece visible to the workgroup.  Every wave gets the same answer.
+    auto first_missing = [&](int x, int p, int hi, int self) {
+        if (tid == 0) {
+            const long long t_end = wall_clock64() + sk.wait_ticks;
+            for (; p <= hi; ++p) {
+                if (p == self) continue;
+                const unsigned long long* f = sk.flags + (x + NUM_XCD * p);
+                bool ok;
+                for (;;) {
+                    ok = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sk.epoch;
+                    if (ok || wall_clock64() >= t_end) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (!ok) break;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_missing = p;
+        }
+        __syncthreads();
+        const int m = __builtin_amdgcn_readfirstlane(s_missing);
+        __syncthreads();  // every wave has read s_missing before it is written again
+        return m;
+    };
+
+    // phase 0: this rank's pieces (pc counts them); then, for its first and
+    // (if any) second tile, the pieces of the tile's other contributors that
+    // are missing, computed here (cur: the next rank to check), and this
+    // rank's share of the tile's reduction.  Only these counters live across
+    // iterations; the run is derived again each time from an opaque copy of
+    // the workgroup index, which keeps the loop's registers out of the K loop.
+    int phase = 0, pc = 0, cur = -1;
+    bool first_item = true;
+    f32x16 acc[MI][NJ];
+    for (;;) {
+        int b = (int)blockIdx.x;
+        asm volatile("" : "+s"(b));
+        const SkRun r = sk_run(sk, b, G);
+        int u, p;  // the piece to compute: rank p's range of tile u
+        if (phase == 0) {
+            if (pc < r.npieces) {
+                u = r.u0 + pc;
+                p = r.j;
+                ++pc;
+            } else {
+                if (r.npieces == 0) break;
+                // Publish: every wave's stores have completed, then the flag,
+                // with release ordering.
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(sk.flags + b, sk.epoch, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                phase = 1;
+                cur = r.first(r.u0);
+                continue;
+            }
+        } else {
+            u = r.u0 + phase - 1;
+            cur = first_missing(r.x, cur, r.last(u), r.j);
+            if (cur > r.last(u)) {
+                int tm, tn;
+                map_tile(r.pos(u), sk.tiles_m, sk.tiles_n, tm, tn);
+                sk_reduce<OUT, EPI, PAIRS>(r.x, r.j, r.W, r.nk, u, tm, tn, sk.part, C, M, N, ldc,
+                                           wave, lane, epi.alpha, epi.beta, epi.bias, epi.relu);
+                if (phase == r.npieces) break;
+                ++phase;
+                cur = r.first(r.u0 + 1);
+                continue;
+            }
+            p = cur++;
+        }
+        if (!first_item) __syncthreads();  // every wave is done with the LDS ring and the slot
+        first_item = false;
+
+        int tm, tn, kb, ke;
+        map_tile(r.pos(u), sk.tiles_m, sk.tiles_n, tm, tn);
+        r.piece(p, u, kb, ke);
+        const int m0 = tm * SK_TILE;
+        const int n0 = tn * SK_TILE;
+        const int rows_a = (M - m0) < SK_TILE ? (M - m0) : SK_TILE;
+        const int cols_b = (N - n0) < SK_TILE ? (N - n0) : SK_TILE;
+        const int kbeg = kb * SK_BK;
+        const int kseg = (ke == r.nk ? K : ke * SK_BK) - kbeg;
+        mainloop16<IN, SK_TILE, SK_TILE, SLAB2, 2, true, true>(
+            A + (int64_t)kbeg * 2, B + (int64_t)kbeg * ldb * 2, kseg, lda, ldb, m0, n0, rows_a, cols_b,
+            smem, acc);
+        part_store<MI, NJ>(acc, sk.part + (int64_t)r.slot(p, u) * SK_SLOT, wave, lane);
+        // A piece computed for another rank is read by this workgroup's waves
+        // in the reduction: the barrier before it (in first_missing) orders them.
+    }
+}
+
+template <int IN, int OUT, bool EPI, bool PAIRS>
+hipError_t go_sk(const GemmLaunch& L, const SkSched& s, int grid) {
+    const char* a = L.A;
+    const char* b = L.B;
+    char* c = L.C;
+    int M = L.M, N = L.N, K = L.K, lda = L.lda, ldb = L.ldb, ldc = L.ldc;
+    SkSched sk = s;
+    EpiArgs e = L.e;
+    void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &sk, &e};
+    return hipLaunchKernel((const void*)gemm16_sk_kernel<IN, OUT, EPI, PAIRS>, dim3((unsigned)grid),
+                           dim3(256), args, 0, L.stream);
+}
+
+template <int IN, int OUT, bool EPI>
+hipError_t sk_by_pairs(const GemmLaunch& L, const SkSched& s, int grid) {
+    if (OUT != OUT_F32 && L.N % 2 == 0) return go_sk<IN, OUT, EPI, true>(L, s, grid);
+    return go_sk<IN, OUT, EPI, false>(L, s, grid);
+}
+
+template <int IN, int OUT>
+hipError_t sk_by_epi(const GemmLaunch& L, const SkSched& s, int grid) {
+    return L.epi ? sk_by_pairs<IN, OUT, true>(L, s, grid) : sk_by_pairs<IN, OUT, false>(L, s, grid);
 }
 
 template <int IN, int OUT, int TBM, int TBN, bool EPI, bool PAIRS, int SCHED, int S>
@@ -508,6 +754,19 @@ hipError_t by_epi(const GemmLaunch& L) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm16_sk(const GemmLaunch& L, const SkSched& s, int grid) {
+    if (L.tbm != SK_TILE || L.tbn != SK_TILE || grid <= 0 || grid % NUM_XCD != 0 || s.nk <= 0)
+        return hipErrorInvalidValue;
+    if (L.in == IN_BF16) {
+        if (L.out == OUT_F32) return sk_by_epi<IN_BF16, OUT_F32>(L, s, grid);
+        if (L.out == OUT_BF16) return sk_by_epi<IN_BF16, OUT_BF16>(L, s, grid);
+    } else if (L.in == IN_F16) {
+        if (L.out == OUT_F32) return sk_by_epi<IN_F16, OUT_F32>(L, s, grid);
+        if (L.out == OUT_F16) return sk_by_epi<IN_F16, OUT_F16>(L, s, grid);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm16(const GemmLaunch& L) {
     if (L.in == IN_BF16) {

@@ -174,6 +174,21 @@ typedef enum {
  * unspecified, and calls that share one workspace must be ordered (same
  * stream).  gemm_ex_plan reports the plan and the bytes it uses.
  *
+ * Stream-K (the nine-levels tutorial, section 2.9: the refinement of Split-K
+ * that gives every thread block the same amount of work): for bf16 / fp16
+ * inputs, when the 256 x 256 tiles do not divide evenly over the 256 CUs
+ * (a last round of tiles that leaves CUs idle), a plan may instead run one
+ * persistent workgroup per CU, each taking an equal run of K steps across
+ * tile boundaries.  Tiles shared by two or more workgroups are finished by the
+ * one holding their last K step, which adds the others' fp32 partial sums (in
+ * the workspace) in a fixed order: results are deterministic for a given
+ * (shape, workspace_bytes) and differ from the other plans' only in fp32
+ * summation order.  It needs 2 x 256 x 256 KiB + 2 KiB of workspace
+ * (128 MiB), and is never used on a stream that is being captured into a
+ * graph (hipStreamIsCapturing).  A workgroup waits a bounded time for a
+ * partial and otherwise computes it itself, so the result does not depend on
+ * how the grid is scheduled.
+ *
  * in:  a dgemm_in code.  out: DGEMM_OUT_F32, or DGEMM_OUT_SAME for C in the
  * input format (for fp32 inputs both mean fp32).  Other arguments,
  * preconditions and errors as the plain entry points.
@@ -217,13 +232,80 @@ int gemm_ex_static(int in, int out, int M, int N, int K,
 
 /*
  * Host-side query of the plan gemm_ex would use with `workspace_bytes`
- * available (no GPU needed): macro-tile shape, split count (1 = unsplit) and
- * the workspace bytes that plan uses (0 when unsplit).  Any output pointer
+ * available (no GPU needed): macro-tile shape, split count (1 = unsplit,
+ * 0 = a Stream-K plan) and the workspace bytes that plan uses (0 when
+ * unsplit).  gemm_ex never takes a Stream-K plan on a stream that is being
+ * captured into a graph; this query assumes no capture.  Any output pointer
  * may be NULL.  Returns DGEMM_OK, or DGEMM_ERR_INVALID_VALUE for negative
  * sizes or a bad `in` / `out`.
  */
 int gemm_ex_plan(int in, int out, int M, int N, int K, size_t workspace_bytes,
                  int* tile_rows, int* tile_cols, int* splits, size_t* workspace_used);
+
+/* Plan kinds of dgemm_set_plan_override. */
+typedef enum {
+    DGEMM_PLAN_AUTO = 0,      /* the cost model's choice (the default)                */
+    DGEMM_PLAN_GRID = 1,      /* one workgroup per tile and K split, as given         */
+    DGEMM_PLAN_STREAM_K = 2,  /* Stream-K (16-bit inputs; 256 x 256 tiles)            */
+    DGEMM_PLAN_NO_STREAM_K = 3 /* the cost model's choice among the other plans       */
+} dgemm_plan_kind;
+
+/*
+ * Process-wide plan override for gemm_ex, gemm_ex_static and gemm_ex_plan,
+ * for tests and for tuning the cost model (the plain entry points ignore it).
+ * DGEMM_PLAN_GRID forces the macro-tile tile_rows x tile_cols (a shape the
+ * input format's kernel has: 256 x 256, 192 x 256 or 128 x 128 for 16-bit
+ * inputs, 128 x 128 for fp32, 256 x 256 or 128 x 128 for 3 x bf16) and
+ * `splits` K pieces (>= 1; reduced to the number of K steps);
+ * DGEMM_PLAN_STREAM_K forces a Stream-K plan, DGEMM_PLAN_NO_STREAM_K rules it
+ * out (tile and split arguments ignored by both).  A forced plan the call cannot take (tile shape the kernel lacks,
+ * workspace too small, Stream-K for fp32 inputs or under graph capture) falls
+ * back to the cost model's choice, which gemm_ex_plan then reports.
+ * DGEMM_PLAN_AUTO clears the override.  Not synchronised with calls running
+ * on other host threads.  Returns DGEMM_OK, or DGEMM_ERR_INVALID_VALUE for a
+ * bad kind or splits < 1 with DGEMM_PLAN_GRID.
+ */
+int dgemm_set_plan_override(int kind, int tile_rows, int tile_cols, int splits);
+
+/*
+ * Process-wide bound on how long a Stream-K workgroup waits for another's
+ * partial sums before computing them itself, in microseconds; us < 0 restores
+ * the default (twice the plan's estimated time plus 100 us), and 0 makes every
+ * workgroup take only what is already there (a test of the fallback path,
+ * whose results are bit for bit those of the waiting path).  Returns DGEMM_OK,
+ * or DGEMM_ERR_INVALID_VALUE for NaN.
+ */
+int dgemm_set_stream_k_wait_us(double us);
+
+/* Item roles reported by dgemm_stream_k_schedule. */
+typedef enum {
+    DGEMM_SK_PIECE = 0,      /* the workgroup's own k range of a tile, summed into `slot`   */
+    DGEMM_SK_RECOMPUTE = 1,  /* another contributor's missing piece, into that one's slot  */
+    DGEMM_SK_REDUCE = 2      /* blocks [lo, hi) of the tile: contributors first .. last
+                                summed in that order, epilogue, stored to C             */
+} dgemm_sk_role;
+
+/*
+ * Host-side query of the Stream-K schedule (no GPU needed; for tests and
+ * tuning): the items workgroup `wg` (0 <= wg < 256; XCD x = wg % 8, rank
+ * wg / 8) of a Stream-K launch runs for an M x N x K GEMM with 16-bit inputs
+ * (`in` = DGEMM_IN_BF16 or DGEMM_IN_F16), in the order it runs them, with
+ * every other contributor's piece already published (partials_present != 0)
+ * or every one missing (0: the workgroup computes each itself).  Each item is
+ * 10 ints in `items`: role (dgemm_sk_role), the tile's row and column index
+ * (256 x 256 tiles), k_begin and k_end (elements of K; PIECE and RECOMPUTE),
+ * the slot (0 .. 511; slots 2 wg and 2 wg + 1 hold workgroup wg's pieces;
+ * -1 for REDUCE), the tile's first and last contributor (ranks of XCD x), and
+ * lo and hi (REDUCE: the tile's 32 x 32 output blocks [lo, hi) of 64, block
+ * q at rows 128 (q / 32) + 32 ((q / 4) % 4), columns 128 ((q / 16) % 2) +
+ * 32 (q % 4) of the tile; 0 otherwise).  *n_items receives the count; only
+ * the first max_items are written.  Returns DGEMM_OK, or
+ * DGEMM_ERR_INVALID_VALUE for a shape Stream-K does not run (other than 16-bit
+ * inputs with at most 256 tiles and at least 32 steps of 64 k per XCD that has
+ * a tile), a bad argument, or max_items below the count.
+ */
+int dgemm_stream_k_schedule(int in, int M, int N, int K, int wg, int partials_present, int* items,
+                            int max_items, int* n_items);
 
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* dgemm_status_string(int status);

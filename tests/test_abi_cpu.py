@@ -288,6 +288,7 @@ def test_plan_without_workspace_is_the_plain_launch(M, N, K, fmt):
     (64, 64, 4096, "f16", None),
     (256, 256, 65536, "bf16", None),
 ])
+@pytest.mark.usefixtures("no_stream_k")
 def test_split_plans(M, N, K, fmt, splits):
     p = dg.gemm_ex_plan(fmt, M, N, K, 1 << 40)
     if splits is not None:
@@ -317,8 +318,15 @@ def test_plan_invariants(M, N, K, fmt, ws):
     tiles = {"f32": {(128, 128)}, "bf16": {(256, 256), (192, 256), (128, 128)},
              "f16": {(256, 256), (192, 256), (128, 128)}, "f32x3": {(256, 256), (128, 128)}}[fmt]
     assert (p["tile_rows"], p["tile_cols"]) in tiles
-    assert 1 <= p["splits"] <= 16
     assert p["workspace_bytes"] <= ws
+    if p["stream_k"]:
+        # one persistent workgroup per CU; two fp32 tiles and a flag each
+        assert fmt in ("bf16", "f16") and M > 0 and N > 0 and K > 0
+        assert (p["tile_rows"], p["tile_cols"], p["splits"]) == (256, 256, 0)
+        assert p["workspace_bytes"] == 2 * 256 * 256 * 256 * 4 + 256 * 8
+        dg.dgemm_stream_k_schedule(fmt, M, N, K, 0)  # a shape the schedule runs
+        return
+    assert 1 <= p["splits"] <= 16
     if p["splits"] == 1:
         assert p["workspace_bytes"] == 0
         t = dg.dgemm_tile_map(M, N, fmt)

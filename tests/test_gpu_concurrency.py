@@ -15,7 +15,7 @@ import torch
 import dense_gemm_matrix_amd as dg
 from synth_inputs import pair, to_torch
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("no_stream_k")]
 
 # (path, M, N, K, C dtype); "f32x3" is fp32 data through the 3 x bf16 split.
 CASES = [

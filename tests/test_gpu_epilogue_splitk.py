@@ -18,7 +18,7 @@ from synth_inputs import draw, pair
 from tests.gpu_util import TORCH, dev_matrix, gap_untouched, round_pitch, sentinel_c, to64
 from synth_inputs import to_torch as to_torch_cpu
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("no_stream_k")]
 
 PATHS = [("f32", "f32"), ("f32x3", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
          ("f16", "f16")]

@@ -19,7 +19,7 @@ import oracle
 from synth_inputs import to_storage
 from tests.gpu_util import dev_matrix, gap_untouched, sentinel_c, to64
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("no_stream_k")]
 
 ENTRY = {"f32": dg.gemm_f32, "f32x3": dg.gemm_f32_3xbf16, "bf16": dg.gemm_bf16, "f16": dg.gemm_f16}
 COMBOS = [("f32", "f32"), ("f32x3", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
