@@ -14,12 +14,13 @@ other parity workloads, and one GPU's row share of the 4096^3
 product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
 the planner splits K, through gemm_ex with a workspace; each both launched call by
 call from Python and replayed from a HIP graph (the small shapes are otherwise
-bound by the host's launch rate).
+bound by the host's launch rate).  "plan_compare" times the cost model's plan
+against a forced Stream-K plan on the shapes with fewer tiles than CUs.
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
-                    [--no-power-clock] [--no-cold-cache] [--no-ceiling] [--vendor]
-                    [--settle-s S]
+                    [--no-power-clock] [--no-cold-cache] [--no-ceiling] [--no-plans]
+                    [--vendor] [--settle-s S]
     python bench.py --copy-calibration      # plain copy of known size, for HBM counters
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
@@ -494,6 +495,48 @@ def other_shapes(dg, args):
     return out
 
 
+PLAN_SHAPES = [("bf16 512x4096x4096 (row share of 4096^3 over 8 GPUs), bf16 C", 512, 4096, 4096),
+               ("bf16 4000x3000x4104, bf16 C", "bf16_4000x3000x4104", 0, 0),
+               ("bf16 2048^3, bf16 C", 2048, 2048, 2048)]
+
+
+def plan_compare(dg, args):
+    """Per shape: gemm_ex with a workspace Stream-K fits in, once with the cost
+    model's plan and once with the Stream-K plan forced (dgemm_set_plan_override),
+    each timed like the other shapes."""
+    import torch
+    from synth_inputs import pair, to_torch, torch_dtype
+    out = []
+    ws = torch.empty(2 * 256 * 256 * 256 * 4 + 256 * 8, dtype=torch.uint8, device="cuda")
+
+    def ex_entry(a, b, c, stream=None):
+        dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
+    try:
+        for label, M, N, K in PLAN_SHAPES:
+            if isinstance(M, str):
+                _, _, Ad, Bd, Cd, meta = device_inputs(M)
+                M, N, K = meta["M"], meta["N"], meta["K"]
+            else:
+                A, B = pair(M, N, K, "normal002", "bf16", seed=6000)
+                Ad, Bd = to_torch(A, "bf16").to("cuda"), to_torch(B, "bf16").to("cuda")
+                Cd = torch.empty((M, N), dtype=torch_dtype("bf16"), device="cuda")
+            print(f"bench: plans {label}", file=sys.stderr, flush=True)
+            steps = max(10, min(args.steps, int(2e4 * 1e9 / gemm_flops(M, N, K))))
+            rec = {"shape": label, "M": M, "N": N, "K": K, "steps": steps}
+            for key, kind in (("cost_model", dg.DGEMM_PLAN_AUTO), ("stream_k", dg.DGEMM_PLAN_STREAM_K)):
+                dg.dgemm_set_plan_override(kind)
+                plan = dg.gemm_ex_plan("bf16", M, N, K, ws.numel(), out_same=True)
+                t, _ = time_gemm(ex_entry, Ad, Bd, Cd, steps, 3, min(args.settle_s, 0.3))
+                rec[key] = {"plan": plan, "us": round(t * 1e6, 2),
+                            "tflops": round(tflops(M, N, K, t), 2)}
+            rec["stream_k_over_cost_model"] = round(rec["stream_k"]["us"] / rec["cost_model"]["us"], 3)
+            out.append(rec)
+            del Ad, Bd, Cd
+    finally:
+        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,6 +555,8 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of launches after the warm-up before each timed block, "
                          "so that timing starts from a settled clock (default 1.0)")
+    ap.add_argument("--no-plans", action="store_true",
+                    help="skip the cost model's plan against forced Stream-K on the under-filled shapes")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -617,6 +662,8 @@ def main():
         line["per_dtype"] = per
     if not args.no_shapes:
         line["other_shapes"] = other_shapes(dg, args)
+    if not args.no_plans:
+        line["plan_compare"] = plan_compare(dg, args)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)
