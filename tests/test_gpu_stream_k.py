@@ -176,6 +176,30 @@ def test_fused_epilogue(stream_k, dtype, out):
         assert gap_untouched(C)
 
 
+@pytest.mark.parametrize("dtype,out,M,N,K", [("bf16", "bf16", 1000, 701, 2100),
+                                             ("f16", "f16", 777, 1023, 4100),
+                                             ("bf16", "f32", 513, 255, 3000)])
+def test_odd_and_ragged_shapes_with_epilogue(stream_k, dtype, out, M, N, K):
+    """Odd N (the per-element store path of 16-bit C), row and column counts
+    one past or short of a tile, K ragged in its last piece; alpha, beta, bias
+    and ReLU; every element against the oracle."""
+    sk_plan(dtype, out, M, N, K)
+    print(f"case sk-odd {dtype}->{out} {M}x{N}x{K}", flush=True)
+    rng = np.random.default_rng(7600 + M + N)
+    A = draw(rng, (M, K), "normal", dtype)
+    B = draw(rng, (K, N), "normal", dtype)
+    Cold = draw(rng, (M, N), "normal", out)
+    bias = rng.standard_normal(N).astype(np.float32)
+    run = Run(dtype, A, B)
+    C = run(out, alpha=-0.5, beta=1.5, Cold=Cold, bias=bias, relu=True)
+    C64, S = oracle.gemm(dtype, A, B)
+    E, T = oracle.epilogue(C64, -0.5, 1.5, oracle.widen(out, Cold), bias.astype(np.float64), True)
+    b = bound_epilogue(E, T, S, -0.5, TOL_MFMA, out)
+    res = oracle.check(to64(C), E, S, TOL_MFMA, out, b=b)
+    assert res["ok"], res
+    assert gap_untouched(C) and run.spare_untouched()
+
+
 def test_launches_sharing_one_workspace(stream_k):
     """Launches of two shapes interleaved on one workspace: each repeats its
     own first result bit for bit (a flag or partial left by another launch is
