@@ -176,18 +176,19 @@ typedef enum {
  *
  * Stream-K (the nine-levels tutorial, section 2.9: the refinement of Split-K
  * that gives every thread block the same amount of work): for bf16 / fp16
- * inputs, when the 256 x 256 tiles do not divide evenly over the 256 CUs
- * (a last round of tiles that leaves CUs idle), a plan may instead run one
+ * inputs with at most 256 tiles of 256 x 256, a plan may instead run one
  * persistent workgroup per CU, each taking an equal run of K steps across
- * tile boundaries.  Tiles shared by two or more workgroups are finished by the
- * one holding their last K step, which adds the others' fp32 partial sums (in
- * the workspace) in a fixed order: results are deterministic for a given
+ * tile boundaries; the workgroups that share a tile then reduce it together,
+ * each adding up its share of the tile's outputs over their fp32 partial sums
+ * (in the workspace) in k order: results are deterministic for a given
  * (shape, workspace_bytes) and differ from the other plans' only in fp32
  * summation order.  It needs 2 x 256 x 256 KiB + 2 KiB of workspace
  * (128 MiB), and is never used on a stream that is being captured into a
  * graph (hipStreamIsCapturing).  A workgroup waits a bounded time for a
  * partial and otherwise computes it itself, so the result does not depend on
- * how the grid is scheduled.
+ * how the grid is scheduled.  On MI355X it measured slower than the other
+ * plans on every shape tried, so the cost model does not pick it; it runs when
+ * forced with dgemm_set_plan_override.
  *
  * in:  a dgemm_in code.  out: DGEMM_OUT_F32, or DGEMM_OUT_SAME for C in the
  * input format (for fp32 inputs both mean fp32).  Other arguments,
