@@ -497,13 +497,15 @@ def other_shapes(dg, args):
 
 PLAN_SHAPES = [("bf16 512x4096x4096 (row share of 4096^3 over 8 GPUs), bf16 C", 512, 4096, 4096),
                ("bf16 4000x3000x4104, bf16 C", "bf16_4000x3000x4104", 0, 0),
-               ("bf16 2048^3, bf16 C", 2048, 2048, 2048)]
+               ("bf16 2048^3, bf16 C", 2048, 2048, 2048),
+               ("bf16 3840x3840x8192 (225 tiles, runs not on tile boundaries), bf16 C", 3840, 3840, 8192)]
 
 
 def plan_compare(dg, args):
     """Per shape: gemm_ex with a workspace Stream-K fits in, once with the cost
     model's plan and once with the Stream-K plan forced (dgemm_set_plan_override),
-    each timed like the other shapes."""
+    each timed like the other shapes: the three shapes with fewer tiles than
+    CUs, and a deep-K one whose Stream-K runs do not start on tile boundaries."""
     import torch
     from synth_inputs import pair, to_torch, torch_dtype
     out = []
