@@ -364,10 +364,10 @@ std::atomic<unsigned long long> g_sk_epoch{
 std::atomic<double> g_sk_wait_us{-1.0};  // < 0: from the estimate
 std::atomic<int> g_wall_khz[256];        // wall-clock rate per device (0: not yet read)
 
-// Longest wait of an owner for one partial, in wall-clock ticks: by default
-// twice the estimated kernel time plus 100 us (a partial is normally long
-// done by then; only a grid that is not co-resident misses it, and the owner
-// then computes it itself).
+// Longest wait of a reducing workgroup for the other contributors' pieces of
+// a tile, in wall-clock ticks: by default twice the estimated kernel time plus
+// 100 us (a piece is normally long done by then; only a grid that is not
+// co-resident misses it, and the reducer then computes it itself).
 long long sk_wait_ticks(double est_us) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) dev = 0;

@@ -522,17 +522,15 @@ __device__ __forceinline__ void part_store(const f32x16 (&acc)[MI][NJ], char* sl
                           acc[mi][nj][4 * c + 3]};
 }
 
+constexpr int SK_BATCH = 8;  // contributors whose partials are loaded ahead of their additions
+
 // This workgroup's share of tile u's reduction: blocks [lo, hi) of the tile,
 // dealt to the four waves in turn.  Each output is the sum of the partials of
 // the tile's contributors first .. last, added in that order, then the
 // epilogue and the one-tile kernel's store of a 32 x 32 block (the
-// accumulator layout the slot keeps).  Loads go out SK_BATCH contributors at
-// a time, ahead of their additions.  Every partial is in its slot and visible
-// to this workgroup.
-constexpr int SK_BATCH = 8;
-
-// A function of its own (arguments in registers), so that its registers are
-// allocated apart from the K loop's.
+// accumulator layout the slot keeps).  Every partial is in its slot and
+// visible to this workgroup.  A function of its own (arguments in registers),
+// so that its registers are allocated apart from the K loop's.
 template <int OUT, bool EPI, bool PAIRS>
 __device__ __attribute__((noinline)) void sk_reduce(int x, int j, int W, int nk, int u, int tm,
                                                     int tn, const char* part, char* C, int M,
@@ -623,7 +621,7 @@ __global__ __launch_bounds__(256) void gemm16_sk_kernel(
         return m;
     };
 
-    // phase 0: this rank's pieces (pc counts them); then, for its first and
+    // Phase 0: this rank's pieces (pc counts them); then, for its first and
     // (if any) second tile, the pieces of the tile's other contributors that
     // are missing, computed here (cur: the next rank to check), and this
     // rank's share of the tile's reduction.  Only these counters live across
