@@ -267,8 +267,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
 
 constexpr int X3_ROW = BK * 2;                  // 64-byte bf16 rows: 4 chunks of 8 k
 
+// Byte offset of chunk c (0..3) of bf16 row r in one part of a stage.  Four
+// 64-byte rows span the 256 bytes of LDS banks, so rows r and r + 4 share
+// banks.  B's transposing stores write rows 4 apart from neighbouring lanes
+// (16 rows per 64-lane store); the fragment reads take 4 consecutive rows at
+// one chunk per group of 4 lanes.  Rows are therefore permuted inside each
+// group of four (slot (r ^ r >> 2) & 3) and chunks XORed with (r >> 2) & 3:
+// the reads still see 4 rows in 4 distinct quarters of the banks, and rows
+// 4 apart now land in different quarters and chunk positions, so 8- and
+// 16-lane groups of either store touch distinct 16-byte bank groups.
 __device__ __forceinline__ int x3_off(int row, int chunk) {
-    return row * X3_ROW + ((chunk ^ ((row ^ (row >> 2)) & 3)) << 4);
+    const int slot = (row & ~3) | ((row ^ (row >> 2)) & 3);
+    return slot * X3_ROW + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 // Split two fp32 values into packed hi and lo bf16 parts (x0 in the low half
