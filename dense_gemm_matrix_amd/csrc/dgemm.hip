@@ -192,14 +192,89 @@ struct Plan {
     int ldw;              // row pitch of the fp32 partials, in elements
     int64_t ws_bytes;     // workspace the plan uses (0 when unsplit)
     int kind = PLAN_GRID;
+    int waves = 0;        // slice-K plans: waves per workgroup (0: a grid plan)
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ slice-K
+//
+// fp32 products whose 128 x 128 grid would leave most CUs idle (at most
+// SLICE_MAX_TILES128 such tiles: 512^3 has 16 for 256 CUs) run the slice-K
+// kernel instead: 32 x 32 or 64 x 64 tiles, K split over the W waves of each
+// workgroup and summed in LDS, so the grid fills the chip without a workspace
+// or a reduction kernel.  Estimated time, fitted to a sweep of 15 shapes from
+// 256^3 to 2048^3 (MI355X; every candidate plan timed by graph replay):
+//
+//   fixed_us + nbw * blk_us * load + (n - 1) * round_us
+//
+// with nbw = the 32-k blocks of one wave (ceil(ceil(K / 32) / W)), n =
+// ceil(tiles / 256) workgroups per CU, and load = 1 for n = 1, else n * co:
+// co < 1 where several workgroups fit on a CU at once (the 4-wave 32 x 32
+// kernel, three per CU) and overlap.  The 32 x 32 tile takes 4 waves (loads
+// spread over the matrix instructions) or 8 (two waves per SIMD; faster once K
+// is deep), whichever is estimated faster; the 64 x 64 tile takes 4.  The tile
+// itself depends on M and N only (the smaller per-block cost of 4 waves), so
+// that dgemm_tile_map stays exact.  Against the grid plans the estimate is
+// compared like any other; in the sweep slice-K was 1.3-2.7x faster than the
+// best grid plan up to 768^3, 1024^3 and deep-K shapes such as 512 x 512 x 8192,
+// and the grid plans kept 1024 x 1024 x 4096 and larger.
+
+constexpr int64_t SLICE_MAX_TILES128 = 64;
+struct SliceCand { int ts, waves; double fixed_us, blk_us, co, round_us; };
+constexpr SliceCand SLICE32_4 = {32, 4, 2.6, 0.9, 0.84, 0.0};
+constexpr SliceCand SLICE32_8 = {32, 8, 3.4, 1.2, 1.0, 2.4};
+constexpr SliceCand SLICE64_4 = {64, 4, 3.5, 2.5, 1.0, 2.2};
+
+bool slice_eligible(int in, int M, int N) {
+    return in == IN_F32 && M > 0 && N > 0 &&
+           ceil_div(M, 128) * ceil_div(N, 128) <= SLICE_MAX_TILES128;
+}
+
+int64_t slice_per_cu(const SliceCand& c, int M, int N) {
+    return ceil_div(ceil_div(M, c.ts) * ceil_div(N, c.ts), NUM_CU);
+}
+
+double slice_load(const SliceCand& c, int64_t n) { return n == 1 ? 1.0 : (double)n * c.co; }
+
+double estimate_slice_us(const SliceCand& c, int M, int N, int K) {
+    const int64_t n = slice_per_cu(c, M, N);
+    const int64_t nbw = ceil_div(ceil_div(K, 32), c.waves);
+    return c.fixed_us + (double)nbw * c.blk_us * slice_load(c, n) + (double)(n - 1) * c.round_us;
+}
+
+// The slice-K tile for M x N (32 or 64): the smaller cost per block of K.
+int slice_tile(int M, int N) {
+    const double c32 = SLICE32_4.blk_us * slice_load(SLICE32_4, slice_per_cu(SLICE32_4, M, N));
+    const double c64 = SLICE64_4.blk_us * slice_load(SLICE64_4, slice_per_cu(SLICE64_4, M, N));
+    return c32 <= c64 ? 32 : 64;
+}
+
+const SliceCand& slice_cand(int ts, int waves) {
+    return ts == 64 ? SLICE64_4 : waves == 8 ? SLICE32_8 : SLICE32_4;
+}
+
+// Waves per workgroup for tile ts: 4 for 64 x 64; for 32 x 32 the faster estimate.
+int slice_waves(int ts, int M, int N, int K) {
+    if (ts == 64) return 4;
+    return estimate_slice_us(SLICE32_8, M, N, K) < estimate_slice_us(SLICE32_4, M, N, K) ? 8 : 4;
+}
+
+Plan slice_plan(int M, int N, int K) {
+    const int ts = slice_tile(M, N);
+    Plan p{ts, ts, 1, K, 0, 0};
+    p.waves = slice_waves(ts, M, N, K);
+    return p;
+}
 
 // Unsplit macro-tile choice: minimise rounds(tiles) x area / eff.  It depends
 // on M, N and the input format only, so the host query reports exactly what
 // an unsplit launch uses.
 TileCand pick_tile(int in, int M, int N) {
+    if (slice_eligible(in, M, N)) {
+        const int ts = slice_tile(M, N);
+        return TileCand{ts, ts, 1.0, 0.0, 1.0};
+    }
     int n = 0;
     const TileCand* cands = tiles_for(in, n);
     TileCand best = cands[0];
@@ -292,13 +367,16 @@ std::atomic<int> g_override_kind{DGEMM_PLAN_AUTO};
 std::atomic<int> g_override_bm{0}, g_override_bn{0}, g_override_splits{1};
 
 Plan make_plan_auto(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool allow_sk) {
+    const bool slice = slice_eligible(in, M, N);
     const TileCand base = pick_tile(in, M, N);
-    Plan plan{base.bm, base.bn, 1, K, 0, 0};
+    Plan plan = slice ? slice_plan(M, N, K) : Plan{base.bm, base.bn, 1, K, 0, 0};
     if (ws_avail == 0 || K == 0 || M == 0 || N == 0) return plan;
     const int bk = bk_of(in);
     const int nk = (int)ceil_div(K, bk);
     const int ldw = (int)ceil_div(N, 4) * 4;
-    double best = estimate_us(in, es_out, M, N, base, 1, nk, ldw) * SPLIT_MARGIN;
+    double best = (slice ? estimate_slice_us(slice_cand(plan.bm, plan.waves), M, N, K)
+                         : estimate_us(in, es_out, M, N, base, 1, nk, ldw)) *
+                  SPLIT_MARGIN;
     int ncand = 0;
     const TileCand* cands = tiles_for(in, ncand);
     for (int c = 0; c < ncand; ++c) {
@@ -333,13 +411,25 @@ Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool 
     if (kind == DGEMM_PLAN_GRID && M > 0 && N > 0) {
         const int bm = g_override_bm.load(std::memory_order_relaxed);
         const int bn = g_override_bn.load(std::memory_order_relaxed);
+        const int ov_splits = g_override_splits.load(std::memory_order_relaxed);
+        // fp32 slice-K tiles: `splits` names the waves per workgroup (1: the
+        // planner's count)
+        if (in == IN_F32 && bm == bn && (bm == 32 || bm == 64) &&
+            ceil_div(M, bm) * ceil_div(N, bm) <= INT32_MAX) {
+            const int waves = ov_splits == 1 ? slice_waves(bm, M, N, K) : ov_splits;
+            if (waves == 4 || (waves == 8 && bm == 32)) {
+                Plan p{bm, bn, 1, K, 0, 0};
+                p.waves = waves;
+                return p;
+            }
+        }
         int n = 0;
         const TileCand* cands = tiles_for(in, n);
         for (int c = 0; c < n; ++c) {
             if (cands[c].bm != bm || cands[c].bn != bn) continue;
             const int bk = bk_of(in);
             const int nk = (int)std::max<int64_t>(ceil_div(K, bk), 1);
-            const int s = std::min(g_override_splits.load(std::memory_order_relaxed), nk);
+            const int s = std::min(ov_splits, nk);
             const int steps = (int)ceil_div(nk, s);
             const int splits = (int)ceil_div(nk, steps);
             const int ldw = (int)ceil_div(N, 4) * 4;
@@ -423,6 +513,7 @@ int run(int in, int outfmt, int M, int N, int K, const void* A, int lda, const v
     // issued three steps ahead) measured 17-27 % faster.
     const int64_t wgs = (int64_t)L.tiles_m * L.tiles_n * p.splits;
     L.stages = (p.bm == 128 && (in == IN_BF16 || in == IN_F16) && wgs <= NUM_CU) ? 4 : 2;
+    L.slice_waves = p.waves;
     if (p.kind == PLAN_STREAM_K) {
         L.out = outfmt;
         L.epi = epi_needed(e);

@@ -58,6 +58,7 @@ struct EpiArgs {
 struct GemmLaunch {
     int in, out, tbm, tbn;
     int stages;  // LDS stages of the 16-bit kernel's 128 x 128 tile (2, or 4 alone on a CU)
+    int slice_waves;  // waves per workgroup of the fp32 slice-K kernel
     bool epi;    // apply `e` in the kernel (only with splits == 1)
     const char* A;
     const char* B;

@@ -637,6 +637,177 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
                                      li, epi);
 }
 
+// ---------------------------------------------------------------- fp32, K sliced over the waves
+//
+// For products whose output is too small to give every CU a 128 x 128 tile
+// (512^3 has 16 of them for 256 CUs), the parallelism that split-K finds in K
+// (the nine-levels tutorial, section 2.9) is found inside the workgroup
+// instead: a workgroup of W waves owns a small TS x TS tile (TS = 32 MI), and
+// its waves split K between them, each an equal run of 32-k blocks, so that
+// every wave holds the whole tile's accumulators for its own k.  The W partial
+// tiles are then added through LDS in wave order and stored by wave 0 with the
+// fused epilogue: no partial sums leave the CU, no workspace is needed and no
+// second kernel runs.  No operand is shared between the waves, so operands go
+// from global memory straight into the registers the matrix instruction reads.
+// For unit u of a block (8 k): lane (g, li) fetches k = 8u + 4g .. 8u + 4g + 3
+// of A's row li as one 16-byte load, and B's element of column li at each of
+// those k as one 4-byte load (each half-wave reads 128 contiguous bytes of a B
+// row); matrix instruction e of the unit then takes k = 8u + e in lanes g = 0
+// and 8u + 4 + e in lanes g = 1, as in gemm32_kernel.  Loads run D - 1 blocks
+// ahead of the matrix instructions in a ring of D register sets, either spread
+// over the previous block's matrix instructions (IL; one wave per SIMD has no
+// other wave to cover a burst of loads) or issued as one burst before them (two
+// waves per SIMD cover each other's bursts, and measured faster so).
+//
+// Edges: A's resource ends after row min(M - m0, TS) - 1 at column K, so rows
+// past M read zeros; a block's B resource ends at its last k-row below K, so
+// k-rows at or past K read zeros, and A's columns at or past K (other data) are
+// zeroed before use in the one block that has them.  Columns past N read other
+// data but feed only outputs that are not stored.
+template <bool EPI, int MI, int W, bool IL>
+__global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
+    const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
+    int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n, EpiArgs epi) {
+    static_assert((MI == 1 || MI == 2) && (W == 4 || W == 8), "tile and waves");
+    constexpr int TS = 32 * MI;
+    constexpr int D = MI == 1 ? 3 : 2;  // register sets in the load ring
+    constexpr int NB = MI * MI;         // 32 x 32 blocks of the tile
+    int tm, tn;
+    map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int lane = (int)threadIdx.x & 63;
+    // wave-uniform (so its k range, B's resources and the loop bounds live in
+    // scalar registers; taken from threadIdx.x it would count as divergent)
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = lane >> 5;
+    const int li = lane & 31;
+    const int m0 = tm * TS;
+    const int n0 = tn * TS;
+    const int rows_a = (M - m0) < TS ? (M - m0) : TS;
+    const int cols_b = (N - n0) < TS ? (N - n0) : TS;
+    const int nblk = (K + 31) / 32;
+    const int kb0 = (int)((int64_t)wave * nblk / W);
+    const int nb = (int)((int64_t)(wave + 1) * nblk / W) - kb0;
+    const int kend = kb0 + nb;
+
+    u32x4 ra[D][MI][4];       // [set][mi][unit]: k 8u + 4g .. + 3 of row mi * 32 + li
+    uint32_t rb[D][MI][4][4]; // [set][nj][unit][e]: k 8u + 4g + e of column nj * 32 + li
+    f32x16 acc[MI][MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < MI; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    // Block kb's resources.  Blocks past this wave's run get empty ones (their
+    // loads return zeros without touching memory), so that every step issues
+    // the same loads on every path and the compiler's load-count waits stay
+    // exact.
+    struct Descs {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto descs = [&](int kb) {
+        const bool live = kb < kend;
+        const int k0 = kb * 32;
+        const int krows = (K - k0) < 32 ? (K - k0) : 32;
+        return Descs{make_rsrc(A + ((int64_t)m0 * lda + k0) * 4,
+                               live ? ((int64_t)(rows_a - 1) * lda + krows) * 4 : 0),
+                     make_rsrc(B + ((int64_t)k0 * ldb + n0) * 4,
+                               live ? ((int64_t)(krows - 1) * ldb + cols_b) * 4 : 0)};
+    };
+    // Load l of a block (A's MI * 4 chunks first, then B's MI * 16 words) into set S.
+    constexpr int NL = MI * 4 + MI * 16;
+    constexpr int NM = 16 * MI * MI;  // matrix instructions per block
+    auto load_one = [&](const Descs& d, int l, auto set) {
+        constexpr int S = decltype(set)::value;
+        if (l < MI * 4) {
+            const int u = l / MI, mi = l % MI;
+            ra[S][mi][u] = load16(d.a, ((mi * 32 + li) * lda + 8 * u + 4 * g) * 4);
+        } else {
+            const int q = l - MI * 4;
+            const int u = q / (4 * MI), e = (q / MI) % 4, nj = q % MI;
+            rb[S][nj][u][e] = __builtin_amdgcn_raw_buffer_load_b32(
+                d.b, ((8 * u + 4 * g + e) * ldb + nj * 32 + li) * 4, 0, 0);
+        }
+    };
+    auto load_block = [&](int kb, auto set) {
+        const Descs d = descs(kb);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) load_one(d, l, set);
+    };
+    // One block from set S, with block kb + D - 1's loads (into the set the
+    // previous block emptied) spread over its matrix instructions.
+    auto step = [&](int kb, auto set) {
+        constexpr int S = decltype(set)::value;
+        using SN = std::integral_constant<int, (S + D - 1) % D>;
+        const Descs nd = descs(kb + D - 1);
+        const int k0 = kb * 32;
+        if (k0 + 32 > K) {  // the block holding K's tail: zero A's columns at or past K
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    ra[S][mi][u] = mask_tail32(ra[S][mi][u], K - (k0 + 8 * u + 4 * g));
+        }
+        if constexpr (!IL) {
+#pragma unroll
+            for (int l = 0; l < NL; ++l) load_one(nd, l, SN{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            const int u = i / (4 * MI * MI), e = (i / (MI * MI)) % 4;
+            const int mi = (i / MI) % MI, nj = i % MI;
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                as_float(ra[S][mi][u][e]), as_float(rb[S][nj][u][e]), acc[mi][nj], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (IL) {
+#pragma unroll
+                for (int l = (i * NL) / NM; l < ((i + 1) * NL) / NM; ++l) load_one(nd, l, SN{});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    load_block(kb0, I0{});
+    if constexpr (D == 3) {
+        load_block(kb0 + 1, I1{});
+        for (int j = 0; j < nb; j += 3) {
+            step(kb0 + j, I0{});
+            if (j + 1 >= nb) break;
+            step(kb0 + j + 1, I1{});
+            if (j + 2 >= nb) break;
+            step(kb0 + j + 2, I2{});
+        }
+    } else {
+        for (int j = 0; j < nb; j += 2) {
+            step(kb0 + j, I0{});
+            if (j + 1 >= nb) break;
+            step(kb0 + j + 1, I1{});
+        }
+    }
+    // The waves' partial tiles, added in wave order by wave 0.
+    __shared__ float red[W - 1][NB * 16][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[wave - 1][b * 16 + r][lane] = acc[b / MI][b % MI][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b / MI][b % MI][r] += red[w][b * 16 + r][lane];
+        store_tile<OUT_F32, MI, MI, EPI, false>(acc, C, M, N, ldc, m0, n0, g, li, epi);
+    }
+}
+
 hipError_t go(const void* fn, const GemmLaunch& L) {
     const char* a = L.A;
     const char* b = L.B;
@@ -650,10 +821,31 @@ hipError_t go(const void* fn, const GemmLaunch& L) {
                            dim3(NTHREADS), args, 0, L.stream);
 }
 
+// Slice-K launches: one workgroup of W waves per TS x TS tile.
+template <int MI, int W, bool IL>
+hipError_t go_slicek(const GemmLaunch& L) {
+    const void* fn = L.epi ? (const void*)gemm32_slicek_kernel<true, MI, W, IL>
+                           : (const void*)gemm32_slicek_kernel<false, MI, W, IL>;
+    const char* a = L.A;
+    const char* b = L.B;
+    char* c = L.C;
+    int M = L.M, N = L.N, K = L.K, lda = L.lda, ldb = L.ldb, ldc = L.ldc;
+    int tiles_m = L.tiles_m, tiles_n = L.tiles_n;
+    EpiArgs e = L.e;
+    void* args[] = {&a, &b, &c, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &e};
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * W), args, 0, L.stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm32(const GemmLaunch& L) {
     if (L.out != OUT_F32 || L.tbm != L.tbn) return hipErrorInvalidValue;
+    if (L.in == IN_F32 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 4)
+        return go_slicek<1, 4, true>(L);
+    if (L.in == IN_F32 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 8)
+        return go_slicek<1, 8, false>(L);
+    if (L.in == IN_F32 && L.splits == 1 && L.tbm == 64 && L.slice_waves == 4)
+        return go_slicek<2, 4, true>(L);
     if (L.in == IN_F32 && L.tbm == 128)
         return go(L.epi ? (const void*)gemm32_kernel<true, 128> : (const void*)gemm32_kernel<false, 128>,
                   L);

@@ -26,7 +26,7 @@ CASES = [
     ("f32", "f32", 200, 136, 300, None, None),
     ("f32x3", "f32", 130, 72, 100, None, None),
     ("ex-bf16", "same", 64, 72, 4104, 0.5, 1),     # a split-K plan with the epilogue
-    ("ex-f32", "f32", 96, 64, 2048, 1.0, 0),       # a split-K plan
+    ("ex-f32", "f32", 96, 64, 2048, 1.0, 0),       # a slice-K plan (no workspace)
     ("ex-f16", "f32", 300, 264, 520, 0.5, 1),
     ("bf16", "f32", 0, 64, 64, None, None),        # empty output: a no-op
     ("f16", "f32", 64, 72, 0, None, None),         # K = 0 writes zeros

@@ -6,7 +6,8 @@ arguments alone, so calls made from several threads on several streams must
 give the same bytes as the same calls made one at a time.  ctypes releases the
 interpreter lock for the duration of each foreign call, so the threads do enter
 the library together.  The cases include split-K plans, whose workspace the
-binding takes from torch's allocator on the calling thread's stream."""
+binding takes from torch's allocator on the calling thread's stream, and fp32
+slice-K plans (K split across the waves of a workgroup)."""
 import threading
 
 import pytest
@@ -21,10 +22,10 @@ pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("no_stream_k")]
 CASES = [
     ("bf16", 300, 264, 520, torch.float32),
     ("f16", 64, 72, 4104, torch.float16),      # a split-K plan
-    ("f32", 257, 132, 300, torch.float32),
+    ("f32", 257, 132, 300, torch.float32),     # slice-K, 4 waves per workgroup
     ("f32x3", 200, 136, 300, torch.float32),
     ("bf16", 512, 512, 1024, torch.bfloat16),
-    ("f32", 96, 64, 2048, torch.float32),      # a split-K plan
+    ("f32", 96, 64, 2048, torch.float32),      # slice-K, 8 waves per workgroup (deep K)
 ]
 ITERS = 25
 
@@ -48,9 +49,10 @@ def test_threads_on_their_own_streams_match_one_at_a_time():
         dt = "f32" if path == "f32x3" else path
         A, B = pair(M, N, K, "uniform", dt, seed=8100 + i)
         inputs.append((to_torch(A, dt).cuda(), to_torch(B, dt).cuda()))
-    plans = [dg.gemm_ex_plan("f16", 64, 72, 4104, 1 << 40, out_same=True),
-             dg.gemm_ex_plan("f32", 96, 64, 2048, 1 << 40)]
-    assert all(p["splits"] > 1 for p in plans), plans
+    assert dg.gemm_ex_plan("f16", 64, 72, 4104, 1 << 40, out_same=True)["splits"] > 1
+    for M, N, K in [(257, 132, 300), (96, 64, 2048)]:
+        p = dg.gemm_ex_plan("f32", M, N, K, 1 << 40)
+        assert (p["tile_rows"], p["splits"]) == (32, 1), p
     refs = [as_bits(launch(c[0], *inputs[i], c[4])).clone() for i, c in enumerate(CASES)]
     torch.cuda.synchronize()
 

@@ -95,7 +95,7 @@ def test_exact_integer_inputs_bitwise(path, out, M, N, K):
 
 # (workload, path, the macro-tile its plain launch uses).  Parametrizations of
 # one workload are adjacent so that the oracle's result is computed once.
-WORKLOAD_RUNS = [("f32_512", "f32", 128), ("f32_512", "f32x3", 128),
+WORKLOAD_RUNS = [("f32_512", "f32", 32), ("f32_512", "f32x3", 128),
                  ("f32_4096", "f32", 128), ("f32_4096", "f32x3", 256),
                  ("bf16_4096", "bf16", 256), ("f16_4096", "f16", 256),
                  ("bf16_16384x4096x4096", "bf16", 256), ("bf16_4000x3000x4104", "bf16", 192)]

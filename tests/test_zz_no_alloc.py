@@ -52,10 +52,23 @@ SEQUENCES = [
 ]
 
 
+# fp32 outputs this small take the slice-K kernel (no scratch): the fp32 call
+# forces the split plan through the plan override.
+FORCED_SPLITS = {("f32", 512, 512, 512): (128, 128, 8)}
+
+
+@pytest.fixture
+def clear_override():
+    yield
+    dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+
+
 @pytest.mark.parametrize("seq", range(len(SEQUENCES)))
-def test_static_scratch_matches_gemm_ex_on_two_calls_in_a_row(seq):
+def test_static_scratch_matches_gemm_ex_on_two_calls_in_a_row(seq, clear_override):
     for i, (path, out, M, N, K, alpha, beta, use_bias, relu) in enumerate(SEQUENCES[seq]):
         budget = dg.DGEMM_STATIC_SCRATCH_BYTES
+        force = FORCED_SPLITS.get((path, M, N, K))
+        dg.dgemm_set_plan_override(*((dg.DGEMM_PLAN_GRID,) + force if force else (dg.DGEMM_PLAN_AUTO,)))
         plan = dg.gemm_ex_plan(path, M, N, K, budget, out_same=(out != "f32"))
         assert plan["splits"] > 1 and plan["workspace_bytes"] <= budget, plan
         print(f"case static seq{seq} call{i} {path}->{out} {M}x{N}x{K} plan {plan}", flush=True)
