@@ -539,6 +539,53 @@ def plan_compare(dg, args):
     return out
 
 
+# fp32 outputs of at most 64 tiles of 128 x 128: the cost model's slice-K plan
+# against the 128 x 128 grid kernel forced unsplit and split (the split count
+# the best of a sweep of 2-16 splits).
+F32_PLAN_SHAPES = [("f32 512^3 (the fp32 512^3 workload's shape)", 512, 512, 512, 8),
+                   ("f32 768^3", 768, 768, 768, 6),
+                   ("f32 1024^3", 1024, 1024, 1024, 4),
+                   ("f32 256x256x4096", 256, 256, 4096, 16)]
+
+
+def plan_compare_f32(dg, args):
+    """Per shape: gemm_ex timed by graph replay (these kernels take a few
+    microseconds, less than the host's per-call cost) with the cost model's
+    plan, and with the 128 x 128 grid kernel forced unsplit and split."""
+    import torch
+    from synth_inputs import pair, to_torch
+    out = []
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+
+    def ex_entry(a, b, c, stream=None):
+        dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
+    try:
+        for label, M, N, K, splits in F32_PLAN_SHAPES:
+            A, B = pair(M, N, K, "uniform", "f32", seed=6100)
+            Ad, Bd = to_torch(A, "f32").to("cuda"), to_torch(B, "f32").to("cuda")
+            Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            print(f"bench: fp32 plans {label}", file=sys.stderr, flush=True)
+            rec = {"shape": label, "M": M, "N": N, "K": K}
+            for key, force in (("cost_model", None), ("grid_128_unsplit", (128, 128, 1)),
+                               ("grid_128_split", (128, 128, splits))):
+                if force:
+                    dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, *force)
+                else:
+                    dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+                plan = dg.gemm_ex_plan("f32", M, N, K, ws.numel())
+                for _ in range(20):
+                    ex_entry(Ad, Bd, Cd)
+                torch.cuda.synchronize()
+                t = min(time_graph(ex_entry, Ad, Bd, Cd, 100) for _ in range(3))
+                rec[key] = {"plan": plan, "graph_us": round(t * 1e6, 2),
+                            "tflops": round(tflops(M, N, K, t), 2)}
+            out.append(rec)
+            del Ad, Bd, Cd
+    finally:
+        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -558,7 +605,8 @@ def main():
                     help="seconds of launches after the warm-up before each timed block, "
                          "so that timing starts from a settled clock (default 1.0)")
     ap.add_argument("--no-plans", action="store_true",
-                    help="skip the cost model's plan against forced Stream-K on the under-filled shapes")
+                    help="skip the cost model's plans against forced Stream-K (bf16) and forced "
+                         "128 x 128 grid plans (small fp32 outputs)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -666,6 +714,7 @@ def main():
         line["other_shapes"] = other_shapes(dg, args)
     if not args.no_plans:
         line["plan_compare"] = plan_compare(dg, args)
+        line["plan_compare_f32"] = plan_compare_f32(dg, args)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)
