@@ -2,8 +2,8 @@
 //
 //   * gemm32_kernel: gfx950 has no reduced-precision (xf32) matrix
 //     instruction, so products use full-precision v_mfma_f32_32x32x2_f32.
-//     Operands are staged through registers (B's k x 4 fp32 blocks are
-//     transposed by register renaming), double-buffered in LDS with BK = 32.
+//     Operands go straight from global memory into a double-buffered LDS
+//     ring (BK = 32) with direct-to-LDS loads; B stays N-contiguous there.
 //   * gemm32x3_kernel: the same data on bf16 matrix instructions, each input
 //     split in two bf16 parts and three products taken per term.
 //
@@ -55,11 +55,23 @@ __device__ __forceinline__ u32x4 mask_tail32(u32x4 v, int valid) {
 }
 
 // Square TB x TB macro-tile (256 or 128), 4 waves in a 2 x 2 layout, each wave
-// (TB/2)^2 = MI x MI blocks of 32 x 32 accumulators.  Staging per step: A is
-// TB rows x 8 chunks, thread -> chunk ac of rows ar0 + 32 i (i < TB / 32); B is
-// 32 k-rows x TB columns, thread -> a block of KB k-rows x 4 columns, KB = 8 at
-// TB = 256 and 4 at TB = 128 (256 blocks either way), transposed on its way
-// through registers so that both operands are stored K-contiguous.
+// (TB/2)^2 = MI x MI blocks of 32 x 32 accumulators.  Both operands go from
+// global memory straight into LDS (direct-to-LDS buffer loads, 16 bytes per
+// lane, lane-linear in LDS), NA = TB / 32 loads of A and as many of B per wave
+// and step:
+//   * A, K-contiguous as in memory: load i of wave w fills rows 8 (w NA + i) ..
+//     + 7 (eight 16-byte chunks per row), lane l taking the global chunk that
+//     belongs in slot l % 8 under lds32_index's swizzle; read with
+//     ds_read_b128, four k of one row per lane.
+//   * B, N-contiguous as in memory (TB / 4 chunks per k-row): load i of wave w
+//     fills k-rows ROWB (w NA + i) .. + ROWB - 1; the chunk slots of k-rows
+//     with bit 2 set are rotated by 8 (32 fp32), so that the two lane halves of
+//     a fragment read, k-rows 4 apart, fall in different LDS banks.  A lane
+//     needs four k of one column: two ds_read2st64_b32, each two k-rows apart
+//     by one row pitch.
+// Where the operands used to pass through registers (B transposed there, then
+// written to LDS), the step now issues no LDS stores, and 4096^3 measured 4 %
+// faster (980 against 1021 us, bitwise the same results).
 template <bool EPI, int TB>
 __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
@@ -67,8 +79,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     int kchunk, int64_t c_zstride, EpiArgs epi) {
     static_assert(TB == 256 || TB == 128, "tile");
     constexpr int MI = TB / 64;               // 32 x 32 blocks per wave per dimension
-    constexpr int NA = TB / 32;               // A chunks per thread per step
-    constexpr int KB = TB == 256 ? 8 : 4;     // B k-rows per thread block
+    constexpr int NA = TB / 32;               // loads of A (and of B) per wave per step
+    constexpr int BCH = TB / 4;               // 16-byte chunks per B k-row
+    constexpr int ROWB = 64 / BCH;            // B k-rows per load
     constexpr int STAGE_CHUNKS = TB * ROW_CHUNKS32;
     split_k_window(A, B, C, K, ldb, kchunk, c_zstride);
     // [stage][operand: 0 = A, 1 = B][chunk]: 2 x 2 x (TB / 8) KiB.
@@ -78,7 +91,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform: the loads' LDS addresses go through M0
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m0 = tm * TB;
     const int n0 = tn * TB;
     const int rows_a = (M - m0) < TB ? (M - m0) : TB;
@@ -86,25 +100,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     const int nk = (K + BK - 1) / BK;
     const bool ragged_k = (K % BK) != 0;
 
-    const int ac = tid & 7;
-    const int ar0 = tid >> 3;
-    const int kb = tid % (BK / KB);
-    const int nb = tid / (BK / KB);
-
-    int voff_a[NA], voff_b[KB];
+    // Global byte offsets of this lane's loads within a step's resources.
+    int voff_a[NA], voff_b[NA];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) voff_a[i] = (ar0 + 32 * i) * lda * 4 + ac * 16;
-#pragma unroll
-    for (int i = 0; i < KB; ++i) voff_b[i] = (kb * KB + i) * ldb * 4 + nb * 16;
+    for (int i = 0; i < NA; ++i) {
+        const int row = (wave * NA + i) * 8 + lane / 8;
+        const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+        voff_a[i] = row * lda * 4 + c * 16;
+        const int k = (wave * NA + i) * ROWB + lane / BCH;
+        const int cb = (lane % BCH - ((k >> 2) & 1) * 8 + BCH) % BCH;
+        voff_b[i] = k * ldb * 4 + cb * 16;
+    }
 
-    u32x4 ra[NA], rb[KB];
-
-    // Global loads of step kt: step_desc makes the two resources, load_one
-    // issues load j (0 .. NLOAD - 1, A's first) so that the main loop can
-    // spread them over matrix instructions, mask_a zeroes A's columns at or
-    // past K on the last step of a ragged K (they hold other data: row
-    // padding or the next row; the matching B rows are zero).
-    constexpr int NLOAD = NA + KB;
+    // Global loads of step kt into LDS stage s: step_desc makes the two
+    // resources, load_one issues load j (0 .. NLOAD - 1, A's first) so that the
+    // main loop can spread them over matrix instructions.
+    constexpr int NLOAD = 2 * NA;
     struct StepDesc {
         __amdgpu_buffer_rsrc_t a, b;
     };
@@ -118,37 +129,31 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
         const int64_t bbytes = rows_b > 0 ? ((int64_t)(rows_b - 1) * ldb + cols_b) * 4 : 0;
         return StepDesc{make_rsrc(abase, abytes), make_rsrc(bbase, bbytes)};
     };
-    auto load_one = [&](const StepDesc& d, int j) {
+    auto load_one = [&](const StepDesc& d, int j, int s) {
         if (j < NA)
-            ra[j] = load16(d.a, voff_a[j]);
+            dma16(d.a, lds_addr((const char*)&lds[s][0][0]) + (wave * NA + j) * 1024, voff_a[j]);
         else
-            rb[j - NA] = load16(d.b, voff_b[j - NA]);
+            dma16(d.b, lds_addr((const char*)&lds[s][1][0]) + (wave * NA + j - NA) * 1024,
+                  voff_b[j - NA]);
     };
-    auto mask_a = [&](int kt) {
-        const int valid = K - kt * BK - ac * 4;
+    // The last step of a ragged K: A's columns at or past K hold other data
+    // (row padding or the next row; B's k-rows past K read as zeros), zeroed in
+    // LDS so that 0 * (NaN or Inf) cannot reach a sum.  Each lane fixes the
+    // chunks its own loads wrote, after waiting for them.
+    auto fix_tail = [&](int kt, int s) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 #pragma unroll
-        for (int i = 0; i < NA; ++i) ra[i] = mask_tail32(ra[i], valid);
-    };
-
-    // Registers -> LDS stage s, in NSTORE pieces: piece i < NA writes A chunk
-    // i; piece NA + 4 h + cc writes B column cc's chunk h (KB K-rows x 4
-    // columns become 4 columns x KB / 4 chunks of 4 K values).
-    constexpr int NSTORE = NA + KB;
-    auto store_one = [&](int s, int p) {
-        if (p < NA) {
-            lds[s][0][lds32_index(ar0 + 32 * p, ac)] = ra[p];
-        } else {
-            const int h = (p - NA) / 4, cc = (p - NA) % 4;
-            u32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = rb[4 * h + e][cc];
-            lds[s][1][lds32_index(nb * 4 + cc, kb * (KB / 4) + h)] = v;
+        for (int i = 0; i < NA; ++i) {
+            const int row = (wave * NA + i) * 8 + lane / 8;
+            const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+            u32x4& v = lds[s][0][(wave * NA + i) * 64 + lane];
+            v = mask_tail32(v, K - kt * BK - c * 4);
         }
     };
 
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int g = lane >> 5;   // lane group: which chunk of a chunk pair
+    const int g = lane >> 5;   // lane group: which 4 k of a chunk pair
     const int li = lane & 31;  // row of A / column of B within a 32-block
 
     f32x16 acc[MI][MI];
@@ -159,19 +164,24 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
-    // Operand fragments for one chunk pair (8 k): lane group g reads chunk
-    // 2 * kp + g of its MI A rows and MI B columns.  Two register sets
-    // alternate so that the reads for pair kp + 1 are in flight while kp computes.
+    // Operand fragments for one chunk pair (8 k): lane group g holds k 8 kp + 4 g
+    // .. + 3 of its MI A rows and MI B columns.  Two register sets alternate so
+    // that the reads for pair kp + 1 are in flight while kp computes.
     u32x4 fa[2][MI], fb[2][MI];
 
     auto read_frags = [&](int s, int kp, u32x4 (&a)[MI], u32x4 (&b)[MI]) {
-        const int ch = 2 * kp + g;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            a[mi] = lds[s][0][lds32_index(wm * (TB / 2) + mi * 32 + li, ch)];
+            a[mi] = lds[s][0][lds32_index(wm * (TB / 2) + mi * 32 + li, 2 * kp + g)];
 #pragma unroll
-        for (int nj = 0; nj < MI; ++nj)
-            b[nj] = lds[s][1][lds32_index(wn * (TB / 2) + nj * 32 + li, ch)];
+        for (int nj = 0; nj < MI; ++nj) {
+            const int n = wn * (TB / 2) + nj * 32 + li;
+            const float* bp = (const float*)&lds[s][1][0] + (8 * kp + 4 * g) * TB +
+                              ((n / 4 + 8 * g) % BCH) * 4 + (n & 3);
+            b[nj] = u32x4{__builtin_bit_cast(uint32_t, bp[0]), __builtin_bit_cast(uint32_t, bp[TB]),
+                          __builtin_bit_cast(uint32_t, bp[2 * TB]),
+                          __builtin_bit_cast(uint32_t, bp[3 * TB])};
+        }
     };
 
     // The MI x MI x 4 matrix instructions of one chunk pair (k-quarter e
@@ -195,23 +205,23 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
     auto nothing = [](int) {};
 
     // Schedule of one K step (stage `cur` in LDS, stage cur ^ 1 being filled),
-    // in issue order: read pair 1; pair 0's matrix instructions, with the
-    // global loads of step kt + 1 spread among them; read pair 2; pair 1; read
-    // pair 3; pair 2, with the register -> LDS stores of step kt + 1 spread
-    // among them (stage cur ^ 1 was last read before the previous barrier);
-    // barrier; read pair 0 of stage cur ^ 1; pair 3 (already in registers),
-    // which covers that read's latency.  sched_barrier keeps the compiler from
-    // sinking the fragment reads down to their uses and from gathering the
-    // loads and stores into blocks, which would stall the matrix pipe.
+    // in issue order: read pair 1; pair 0's matrix instructions, with the loads
+    // of step kt + 1 into stage cur ^ 1 spread among them (that stage's last
+    // reads were retired before the previous barrier); read pair 2; pair 1;
+    // read pair 3; pair 2; wait for this wave's loads, barrier; read pair 0 of
+    // stage cur ^ 1; pair 3 (already in registers), which covers that read's
+    // latency.  The loads are inline assembly the compiler does not count, so
+    // the waits before each barrier are explicit.  sched_barrier keeps the
+    // compiler from sinking the fragment reads down to their uses and from
+    // gathering the loads into a block, which would stall the matrix pipe.
     if (nk > 0) {
         {
             const StepDesc d0 = step_desc(0);
 #pragma unroll
-            for (int j = 0; j < NLOAD; ++j) load_one(d0, j);
-            if (ragged_k && nk == 1) mask_a(0);
-#pragma unroll
-            for (int p = 0; p < NSTORE; ++p) store_one(0, p);
+            for (int j = 0; j < NLOAD; ++j) load_one(d0, j, 0);
+            if (ragged_k && nk == 1) fix_tail(0, 0);
         }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
         __syncthreads();
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
             __builtin_amdgcn_sched_barrier(0);
             mfma_frags(fa[0], fb[0], [&](int i) {
 #pragma unroll
-                for (int j = (i * NLOAD) / NMP; j < ((i + 1) * NLOAD) / NMP; ++j) load_one(nd, j);
+                for (int j = (i * NLOAD) / NMP; j < ((i + 1) * NLOAD) / NMP; ++j) load_one(nd, j, cur ^ 1);
             });
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur, 2, fa[0], fb[0]);
@@ -231,13 +241,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm32_kernel(
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur, 3, fa[1], fb[1]);
             __builtin_amdgcn_sched_barrier(0);
-            if (ragged_k && kt + 2 == nk) mask_a(kt + 1);
+            if (ragged_k && kt + 2 == nk) fix_tail(kt + 1, cur ^ 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_frags(fa[0], fb[0], [&](int i) {
-#pragma unroll
-                for (int p = (i * NSTORE) / NMP; p < ((i + 1) * NSTORE) / NMP; ++p) store_one(cur ^ 1, p);
-            });
+            mfma_frags(fa[0], fb[0], nothing);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
             __syncthreads();
             if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
