@@ -653,9 +653,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 // instead: a workgroup of W waves owns a small TS x TS tile (TS = 32 MI), and
 // its waves split K between them, each an equal run of 32-k blocks, so that
 // every wave holds the whole tile's accumulators for its own k.  The W partial
-// tiles are then added through LDS in wave order and stored by wave 0 with the
-// fused epilogue: no partial sums leave the CU, no workspace is needed and no
-// second kernel runs.  No operand is shared between the waves, so operands go
+// tiles are then added through LDS in wave order, each wave summing and storing
+// (with the fused epilogue) an equal share of the tile: no partial sums leave
+// the CU, no workspace is needed and no second kernel runs.  No operand is shared between the waves, so operands go
 // from global memory straight into the registers the matrix instruction reads.
 // For unit u of a block (8 k): lane (g, li) fetches k = 8u + 4g .. 8u + 4g + 3
 // of A's row li as one 16-byte load, and B's element of column li at each of
@@ -797,22 +797,38 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
             step(kb0 + j + 1, I1{});
         }
     }
-    // The waves' partial tiles, added in wave order by wave 0.
-    __shared__ float red[W - 1][NB * 16][64];
-    if (wave > 0) {
+    // The waves' partial tiles, added in wave order (wave 0's first), each
+    // wave summing and storing its share of the tile's accumulator registers:
+    // value idx = 16 b + r (block b, register r) of every lane, for idx in
+    // [wave PER, wave PER + PER).  Register r of lane (g, li) in block b is
+    // row 32 (b / MI) + 8 (r / 4) + 4 g + r % 4, column 32 (b % MI) + li of
+    // the tile; stores go through a buffer resource from the tile's corner to
+    // the end of C, so rows past M fall outside it, and columns past N get an
+    // offset outside any range (the common epilogue's scheme).
+    constexpr int PER = NB * 16 / W;
+    __shared__ float red[W][NB * 16][64];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[wave - 1][b * 16 + r][lane] = acc[b / MI][b % MI][r];
-    }
+        for (int r = 0; r < 16; ++r) red[wave][b * 16 + r][lane] = acc[b / MI][b % MI][r];
     __syncthreads();
-    if (wave == 0) {
-        for (int w = 0; w < W - 1; ++w)
+    const __amdgpu_buffer_rsrc_t cr = c_rsrc(C, M, N, ldc, m0, n0, 4);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+    for (int q = 0; q < PER; ++q) {
+        const int idx = wave * PER + q;
+        const int b = idx / 16, r = idx % 16;
+        float v = red[0][idx][lane];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[b / MI][b % MI][r] += red[w][b * 16 + r][lane];
-        store_tile<OUT_F32, MI, MI, EPI, false>(acc, C, M, N, ldc, m0, n0, g, li, epi);
+        for (int w = 1; w < W; ++w) v += red[w][idx][lane];
+        const int cl = (b % MI) * 32 + li;   // column within the tile
+        const uint32_t off =
+            (n0 + cl < N ? (uint32_t)((4 * g * ldc + cl) * 4) : OOB_LANE) +
+            (uint32_t)(((b / MI) * 32 + 8 * (r >> 2) + (r & 3)) * ldc * 4);
+        if constexpr (EPI) {
+            const float bias = (epi.bias && n0 + cl < N) ? epi.bias[n0 + cl] : 0.0f;
+            v = epilogue_rs<OUT_F32>(v, cr, off, bias, epi);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), cr, (int)off, 0, 0);
     }
 }
 
