@@ -199,36 +199,57 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ slice-K
 //
-// fp32 products whose 128 x 128 grid would leave most CUs idle (at most
-// SLICE_MAX_TILES128 such tiles: 512^3 has 16 for 256 CUs) run the slice-K
-// kernel instead: 32 x 32 or 64 x 64 tiles, K split over the W waves of each
-// workgroup and summed in LDS, so the grid fills the chip without a workspace
-// or a reduction kernel.  Estimated time, fitted to a sweep of 15 shapes from
-// 256^3 to 2048^3 (MI355X; every candidate plan timed by graph replay):
+// fp32 and 3 x bf16 products whose 128 x 128 grid would leave most CUs idle
+// (512^3 has 16 such tiles for 256 CUs) run the slice-K kernel instead: 32 x 32
+// or 64 x 64 tiles, K split over the W waves of each workgroup and summed in
+// LDS, so the grid fills the chip without a workspace or a reduction kernel.
+// Estimated time, per input format and candidate, fitted to a sweep of 22
+// shapes from 128^3 to 2048^2 x 1024 (MI355X; every candidate plan timed by
+// graph replay; worst error 4.5-14 %):
 //
 //   fixed_us + nbw * blk_us * load + (n - 1) * round_us
 //
 // with nbw = the 32-k blocks of one wave (ceil(ceil(K / 32) / W)), n =
 // ceil(tiles / 256) workgroups per CU, and load = 1 for n = 1, else n * co:
 // co < 1 where several workgroups fit on a CU at once (the 4-wave 32 x 32
-// kernel, three per CU) and overlap.  The 32 x 32 tile takes 4 waves (loads
-// spread over the matrix instructions) or 8 (two waves per SIMD; faster once K
-// is deep), whichever is estimated faster; the 64 x 64 tile takes 4.  The tile
-// itself depends on M and N only (the smaller per-block cost of 4 waves), so
-// that dgemm_tile_map stays exact.  Against the grid plans the estimate is
-// compared like any other; in the sweep slice-K was 1.3-2.7x faster than the
-// best grid plan up to 768^3, 1024^3 and deep-K shapes such as 512 x 512 x 8192,
-// and the grid plans kept 1024 x 1024 x 4096 and larger.
+// kernel) and overlap.  The 32 x 32 tile takes 4 waves (loads spread over the
+// matrix instructions) or 8 (two waves per SIMD; faster once K is deep),
+// whichever is estimated faster; the 64 x 64 tile takes 4.  The tile itself
+// depends on M and N only (the smaller per-block cost of 4 waves), so that
+// dgemm_tile_map stays exact.  Against the grid plans the estimate is compared
+// like any other: in the sweep slice-K was 1.3-5x faster than the best grid
+// plan on small outputs and deep-K shapes without a workspace (3 x bf16 512^3
+// 5.2 against 13.1 us, 512 x 512 x 4096 23 against 109 us unsplit), and split-K
+// kept the deepest shapes when a workspace is offered (256 x 256 x 8192 3 x bf16
+// 25.5 against 40 us).
 
-constexpr int64_t SLICE_MAX_TILES128 = 64;
 struct SliceCand { int ts, waves; double fixed_us, blk_us, co, round_us; };
-constexpr SliceCand SLICE32_4 = {32, 4, 2.6, 0.9, 0.84, 0.0};
-constexpr SliceCand SLICE32_8 = {32, 8, 3.4, 1.2, 1.0, 2.4};
-constexpr SliceCand SLICE64_4 = {64, 4, 3.5, 2.5, 1.0, 2.2};
+// fp32 matrix instruction: 32 x 32 with 4 or 8 waves, 64 x 64 with 4.
+constexpr SliceCand SLICE_F32[] = {{32, 4, 2.4, 0.9, 0.82, 0.1},
+                                   {32, 8, 2.7, 1.35, 1.0, 1.6},
+                                   {64, 4, 3.7, 2.27, 1.0, 4.6}};
+// 3 x bf16: the same tiles.
+constexpr SliceCand SLICE_X3[] = {{32, 4, 2.4, 0.72, 0.86, 0.1},
+                                  {32, 8, 2.5, 1.19, 1.0, 1.6},
+                                  {64, 4, 3.6, 1.28, 1.04, 2.9}};
+
+bool slice_format(int in) { return in == IN_F32 || in == IN_F32X3; }
+
+const SliceCand* slice_cands(int in, int& n) {
+    n = 3;
+    return in == IN_F32X3 ? SLICE_X3 : SLICE_F32;
+}
+
+// Largest output, in 128 x 128 tiles, that takes slice-K: for fp32 up to 144
+// (1536^2; at 1024 x 2048 x 1024 44 against 67 us for the grid, at 1536^3 79
+// against 98 us; at 2048^2 x 1024 the grid is faster, 69 against 89 us); for
+// 3 x bf16, whose grid kernel is five times faster per tile, up to 64 (at 128
+// and 144 tiles the two were within 10 % either way).
+int64_t slice_max_tiles128(int in) { return in == IN_F32 ? 144 : 64; }
 
 bool slice_eligible(int in, int M, int N) {
-    return in == IN_F32 && M > 0 && N > 0 &&
-           ceil_div(M, 128) * ceil_div(N, 128) <= SLICE_MAX_TILES128;
+    return slice_format(in) && M > 0 && N > 0 &&
+           ceil_div(M, 128) * ceil_div(N, 128) <= slice_max_tiles128(in);
 }
 
 int64_t slice_per_cu(const SliceCand& c, int M, int N) {
@@ -243,27 +264,46 @@ double estimate_slice_us(const SliceCand& c, int M, int N, int K) {
     return c.fixed_us + (double)nbw * c.blk_us * slice_load(c, n) + (double)(n - 1) * c.round_us;
 }
 
-// The slice-K tile for M x N (32 or 64): the smaller cost per block of K.
-int slice_tile(int M, int N) {
-    const double c32 = SLICE32_4.blk_us * slice_load(SLICE32_4, slice_per_cu(SLICE32_4, M, N));
-    const double c64 = SLICE64_4.blk_us * slice_load(SLICE64_4, slice_per_cu(SLICE64_4, M, N));
-    return c32 <= c64 ? 32 : 64;
+// The candidate of format `in` with tile ts and `waves` waves (nullptr: none).
+const SliceCand* slice_cand(int in, int ts, int waves) {
+    int n = 0;
+    const SliceCand* c = slice_cands(in, n);
+    for (int i = 0; i < n; ++i)
+        if (c[i].ts == ts && c[i].waves == waves) return &c[i];
+    return nullptr;
 }
 
-const SliceCand& slice_cand(int ts, int waves) {
-    return ts == 64 ? SLICE64_4 : waves == 8 ? SLICE32_8 : SLICE32_4;
+// The slice-K tile for M x N (32 or 64): the smaller cost per block of K of
+// the 4-wave candidates.  It depends on M and N only, so that dgemm_tile_map
+// stays exact.
+int slice_tile(int in, int M, int N) {
+    const SliceCand& c32 = *slice_cand(in, 32, 4);
+    const SliceCand& c64 = *slice_cand(in, 64, 4);
+    return c32.blk_us * slice_load(c32, slice_per_cu(c32, M, N)) <=
+                   c64.blk_us * slice_load(c64, slice_per_cu(c64, M, N))
+               ? 32
+               : 64;
 }
 
-// Waves per workgroup for tile ts: 4 for 64 x 64; for 32 x 32 the faster estimate.
-int slice_waves(int ts, int M, int N, int K) {
-    if (ts == 64) return 4;
-    return estimate_slice_us(SLICE32_8, M, N, K) < estimate_slice_us(SLICE32_4, M, N, K) ? 8 : 4;
+// Waves per workgroup for tile ts: the faster estimate among the format's
+// candidates of that tile.
+int slice_waves(int in, int ts, int M, int N, int K) {
+    int n = 0;
+    const SliceCand* c = slice_cands(in, n);
+    int best = 0;
+    double best_us = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (c[i].ts != ts) continue;
+        const double us = estimate_slice_us(c[i], M, N, K);
+        if (best == 0 || us < best_us) { best = c[i].waves; best_us = us; }
+    }
+    return best;
 }
 
-Plan slice_plan(int M, int N, int K) {
-    const int ts = slice_tile(M, N);
+Plan slice_plan(int in, int M, int N, int K) {
+    const int ts = slice_tile(in, M, N);
     Plan p{ts, ts, 1, K, 0, 0};
-    p.waves = slice_waves(ts, M, N, K);
+    p.waves = slice_waves(in, ts, M, N, K);
     return p;
 }
 
@@ -272,7 +312,7 @@ Plan slice_plan(int M, int N, int K) {
 // an unsplit launch uses.
 TileCand pick_tile(int in, int M, int N) {
     if (slice_eligible(in, M, N)) {
-        const int ts = slice_tile(M, N);
+        const int ts = slice_tile(in, M, N);
         return TileCand{ts, ts, 1.0, 0.0, 1.0};
     }
     int n = 0;
@@ -369,12 +409,12 @@ std::atomic<int> g_override_bm{0}, g_override_bn{0}, g_override_splits{1};
 Plan make_plan_auto(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool allow_sk) {
     const bool slice = slice_eligible(in, M, N);
     const TileCand base = pick_tile(in, M, N);
-    Plan plan = slice ? slice_plan(M, N, K) : Plan{base.bm, base.bn, 1, K, 0, 0};
+    Plan plan = slice ? slice_plan(in, M, N, K) : Plan{base.bm, base.bn, 1, K, 0, 0};
     if (ws_avail == 0 || K == 0 || M == 0 || N == 0) return plan;
     const int bk = bk_of(in);
     const int nk = (int)ceil_div(K, bk);
     const int ldw = (int)ceil_div(N, 4) * 4;
-    double best = (slice ? estimate_slice_us(slice_cand(plan.bm, plan.waves), M, N, K)
+    double best = (slice ? estimate_slice_us(*slice_cand(in, plan.bm, plan.waves), M, N, K)
                          : estimate_us(in, es_out, M, N, base, 1, nk, ldw)) *
                   SPLIT_MARGIN;
     int ncand = 0;
@@ -412,12 +452,12 @@ Plan make_plan(int in, int es_out, int M, int N, int K, uint64_t ws_avail, bool 
         const int bm = g_override_bm.load(std::memory_order_relaxed);
         const int bn = g_override_bn.load(std::memory_order_relaxed);
         const int ov_splits = g_override_splits.load(std::memory_order_relaxed);
-        // fp32 slice-K tiles: `splits` names the waves per workgroup (1: the
-        // planner's count)
-        if (in == IN_F32 && bm == bn && (bm == 32 || bm == 64) &&
+        // fp32 and 3 x bf16 slice-K tiles: `splits` names the waves per
+        // workgroup (1: the planner's count)
+        if (slice_format(in) && bm == bn && (bm == 32 || bm == 64) &&
             ceil_div(M, bm) * ceil_div(N, bm) <= INT32_MAX) {
-            const int waves = ov_splits == 1 ? slice_waves(bm, M, N, K) : ov_splits;
-            if (waves == 4 || (waves == 8 && bm == 32)) {
+            const int waves = ov_splits == 1 ? slice_waves(in, bm, M, N, K) : ov_splits;
+            if (slice_cand(in, bm, waves)) {
                 Plan p{bm, bn, 1, K, 0, 0};
                 p.waves = waves;
                 return p;

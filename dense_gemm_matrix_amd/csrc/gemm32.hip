@@ -303,6 +303,18 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
 }
 
+// Split eight fp32 values (x, then y) into packed bf16 hi and lo parts, value
+// j in half j % 2 of word j / 2.
+__device__ __forceinline__ void split8(u32x4 x, u32x4 y, u32x4& hi, u32x4& lo) {
+    uint32_t h[4], l[4];
+    split_pair(as_float(x[0]), as_float(x[1]), h[0], l[0]);
+    split_pair(as_float(x[2]), as_float(x[3]), h[1], l[1]);
+    split_pair(as_float(y[0]), as_float(y[1]), h[2], l[2]);
+    split_pair(as_float(y[2]), as_float(y[3]), h[3], l[3]);
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Square TB x TB macro-tile (256 or 128), 4 waves in a 2 x 2 layout, each
 // wave (TB/2)^2 = MI x MI blocks of 32 x 32 accumulators.  Staging per step
 // (BK = 32): A is TB rows, thread -> 8 consecutive k (two 16-byte fp32
@@ -655,31 +667,124 @@ __global__ __launch_bounds__(NTHREADS) void gemm32x3_kernel(
 // every wave holds the whole tile's accumulators for its own k.  The W partial
 // tiles are then added through LDS in wave order, each wave summing and storing
 // (with the fused epilogue) an equal share of the tile: no partial sums leave
-// the CU, no workspace is needed and no second kernel runs.  No operand is shared between the waves, so operands go
-// from global memory straight into the registers the matrix instruction reads.
-// For unit u of a block (8 k): lane (g, li) fetches k = 8u + 4g .. 8u + 4g + 3
-// of A's row li as one 16-byte load, and B's element of column li at each of
-// those k as one 4-byte load (each half-wave reads 128 contiguous bytes of a B
-// row); matrix instruction e of the unit then takes k = 8u + e in lanes g = 0
-// and 8u + 4 + e in lanes g = 1, as in gemm32_kernel.  Loads run D - 1 blocks
-// ahead of the matrix instructions in a ring of D register sets, either spread
-// over the previous block's matrix instructions (IL; one wave per SIMD has no
-// other wave to cover a burst of loads) or issued as one burst before them (two
-// waves per SIMD cover each other's bursts, and measured faster so).
+// the CU, no workspace is needed and no second kernel runs.
+//
+// No operand is shared between the waves, so each wave moves its own.  For
+// unit u of a block (8 k):
+//   * A: lane (g, li) fetches k = 8u + 4g .. 8u + 4g + 3 of A's row li as one
+//     16-byte load into registers.
+//   * B at TS = 32: lane (g, li) fetches its column's element at each of
+//     those k with a 4-byte load (each half-wave reads 128 contiguous bytes of
+//     a B row), 16 per block.
+//   * B at TS = 64 (BL): 32 such loads per block would keep the CU's texture
+//     addresser, which costs the same per load instruction whatever its width,
+//     busier than the matrix work; the block's 32 k-rows x 64 columns go
+//     instead into the wave's own LDS region as they lie in memory, with eight
+//     16-byte direct-to-LDS loads, and lane (g, li) reads its column's values
+//     back (ds_read2st64 pairs, two k-rows per instruction): 10-17 % faster
+//     per block.  The two lane halves read k-rows 4 apart, which share LDS
+//     banks; a layout that separated them would give the halves different
+//     offsets, and the 2-way conflict costs less than those few reads' issue.
+//     At TS = 32 the same route measured no faster (a 16-k deep product's
+//     latency is mostly the LDS round trip's).
+// Matrix instruction e of unit u then takes k = 8u + e in lanes g = 0 and
+// 8u + 4 + e in lanes g = 1, as in gemm32_kernel.  Loads run D - 1 blocks
+// ahead of the matrix instructions (a ring of register sets, and for BL of
+// LDS stages), either spread over the previous block's matrix instructions
+// (IL; one wave per SIMD has no other wave to cover a burst of loads) or
+// issued as one burst before them (two waves per SIMD cover each other's
+// bursts).  Every block issues the same NL loads, so before a block's B
+// values are read from LDS, exactly (D - 2) NL younger loads may still be
+// outstanding; the read (read_b_frags) waits for that count itself, since the
+// compiler, which tracks which LDS array each direct-to-LDS load writes, loses
+// that across the loop's back edge and would wait for every load.
 //
 // Edges: A's resource ends after row min(M - m0, TS) - 1 at column K, so rows
 // past M read zeros; a block's B resource ends at its last k-row below K, so
 // k-rows at or past K read zeros, and A's columns at or past K (other data) are
 // zeroed before use in the one block that has them.  Columns past N read other
 // data but feed only outputs that are not stored.
-template <bool EPI, int MI, int W, bool IL>
+//
+// X3: the same loads feed the 3 x bf16 products instead (gemm32x3_kernel's
+// arithmetic).  Per block and 16-k half h, lane (g, li) splits its eight fp32
+// values of A's row (units 2h and 2h + 1) and of B's column (the same k) into
+// bf16 hi and lo parts; operand slot j < 4 holds k = 16h + 4g + j and slot
+// j >= 4 holds k = 16h + 8 + 4g + j - 4, in A and in B alike, so each
+// v_mfma_f32_32x32x16_bf16 sums the half's 16 k.  Per 32 x 32 block three
+// products, the small terms first (lo.hi, hi.lo, hi.hi).  Half 1's split is
+// issued between half 0's matrix instructions.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One direct-to-LDS 16-byte-per-lane buffer load through the compiler's
+// builtin (which, unlike dma16, the compiler counts, so its own load-count
+// waits stay exact): lane l's 16 bytes from voffset land at dst + 16 l.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, float* dst, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                             voffset, 0, 0, 0);
+}
+
+// Lane (g, li)'s B values of one 32 x 64 block from its wave's LDS stage
+// (k-row r at r * 64 floats; `base` = the byte address of k-row 4g, column
+// li): rb[nj][u][e] = k-row 8u + 4g + e, column 32 nj + li.  One asm
+// statement that first waits until at most VM of this wave's vector-memory
+// loads are outstanding (so the stage's direct-to-LDS loads have landed) and
+// waits for its own reads before it ends, so that no read is in flight when
+// the compiler takes the output registers as written.
+template <int VM>
+__device__ __forceinline__ void read_b_frags64(uint32_t base, uint32_t (&rb)[2][4][4]) {
+    // k-row 8u + e is 8u + e rows of 64 floats from base; column block nj
+    // 32 floats on.
+    u32x2 p[16];
+    asm volatile(
+        "s_waitcnt vmcnt(%18)\n\t"
+        "ds_read2st64_b32 %0, %16 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %16 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %16 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b32 %3, %16 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b32 %4, %16 offset0:16 offset1:17\n\t"
+        "ds_read2st64_b32 %5, %16 offset0:18 offset1:19\n\t"
+        "ds_read2st64_b32 %6, %16 offset0:24 offset1:25\n\t"
+        "ds_read2st64_b32 %7, %16 offset0:26 offset1:27\n\t"
+        "ds_read2st64_b32 %8, %17 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %9, %17 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %10, %17 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b32 %11, %17 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b32 %12, %17 offset0:16 offset1:17\n\t"
+        "ds_read2st64_b32 %13, %17 offset0:18 offset1:19\n\t"
+        "ds_read2st64_b32 %14, %17 offset0:24 offset1:25\n\t"
+        "ds_read2st64_b32 %15, %17 offset0:26 offset1:27\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]),
+          "=v"(p[7]), "=v"(p[8]), "=v"(p[9]), "=v"(p[10]), "=v"(p[11]), "=v"(p[12]),
+          "=v"(p[13]), "=v"(p[14]), "=v"(p[15])
+        : "v"(base), "v"(base + 128), "n"(VM)
+        : "memory");
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            rb[nj][u][0] = p[8 * nj + 2 * u][0];
+            rb[nj][u][1] = p[8 * nj + 2 * u][1];
+            rb[nj][u][2] = p[8 * nj + 2 * u + 1][0];
+            rb[nj][u][3] = p[8 * nj + 2 * u + 1][1];
+        }
+}
+
+template <bool EPI, int MI, int W, bool IL, bool X3>
 __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
     const char* __restrict__ A, const char* __restrict__ B, char* __restrict__ C,
     int M, int N, int K, int lda, int ldb, int ldc, int tiles_m, int tiles_n, EpiArgs epi) {
     static_assert((MI == 1 || MI == 2) && (W == 4 || W == 8), "tile and waves");
     constexpr int TS = 32 * MI;
-    constexpr int D = MI == 1 ? 3 : 2;  // register sets in the load ring
+    constexpr int D = MI == 1 ? 3 : 2;  // blocks in the load ring
     constexpr int NB = MI * MI;         // 32 x 32 blocks of the tile
+    constexpr bool BL = MI == 2;        // B through LDS
+    constexpr int BLK = 32 * TS;        // fp32 of one wave's B block
+    constexpr int NLB = BL ? BLK / 256 : MI * 16;  // B loads per block
+    __shared__ __attribute__((aligned(1024))) float lb0[BL ? W * BLK : 4];
+    __shared__ __attribute__((aligned(1024))) float lb1[BL ? W * BLK : 4];
+    __shared__ __attribute__((aligned(1024))) float lb2[BL && D == 3 ? W * BLK : 4];
+    __shared__ __attribute__((aligned(16))) float red[W * NB * 16 * 64];
     int tm, tn;
     map_tile((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int lane = (int)threadIdx.x & 63;
@@ -697,8 +802,18 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
     const int nb = (int)((int64_t)(wave + 1) * nblk / W) - kb0;
     const int kend = kb0 + nb;
 
-    u32x4 ra[D][MI][4];       // [set][mi][unit]: k 8u + 4g .. + 3 of row mi * 32 + li
-    uint32_t rb[D][MI][4][4]; // [set][nj][unit][e]: k 8u + 4g + e of column nj * 32 + li
+    // BL: global offset (bytes, from the block's corner) that direct-to-LDS
+    // load j of this lane fetches: the 4 floats that belong at floats
+    // 256 j + 4 lane of the wave's stage.
+    int voff_b[BL ? NLB : 1];
+#pragma unroll
+    for (int j = 0; j < (BL ? NLB : 0); ++j) {
+        const int q = 256 * j + 4 * lane;
+        voff_b[j] = ((q / TS) * ldb + q % TS) * 4;
+    }
+
+    u32x4 ra[D][MI][4];     // [stage][mi][unit]: k 8u + 4g .. + 3 of row mi * 32 + li
+    uint32_t rbr[BL ? 1 : D][MI][4][4];  // !BL: [stage][nj][unit][e]: k 8u + 4g + e of column nj * 32 + li
     f32x16 acc[MI][MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -707,6 +822,10 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
 
+    auto stage = [&](auto set) -> float* {
+        constexpr int S = decltype(set)::value;
+        return (S == 0 ? lb0 : S == 1 ? lb1 : lb2) + wave * BLK;
+    };
     // Block kb's resources.  Blocks past this wave's run get empty ones (their
     // loads return zeros without touching memory), so that every step issues
     // the same loads on every path and the compiler's load-count waits stay
@@ -723,18 +842,21 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
                      make_rsrc(B + ((int64_t)k0 * ldb + n0) * 4,
                                live ? ((int64_t)(krows - 1) * ldb + cols_b) * 4 : 0)};
     };
-    // Load l of a block (A's MI * 4 chunks first, then B's MI * 16 words) into set S.
-    constexpr int NL = MI * 4 + MI * 16;
-    constexpr int NM = 16 * MI * MI;  // matrix instructions per block
+    // Load l of a block into stage S: A's MI * 4 chunks first, then B's NLB.
+    constexpr int NL = MI * 4 + NLB;
+    constexpr int NM = (X3 ? 6 : 16) * MI * MI;  // matrix instructions per block
     auto load_one = [&](const Descs& d, int l, auto set) {
         constexpr int S = decltype(set)::value;
         if (l < MI * 4) {
             const int u = l / MI, mi = l % MI;
             ra[S][mi][u] = load16(d.a, ((mi * 32 + li) * lda + 8 * u + 4 * g) * 4);
+        } else if constexpr (BL) {
+            const int j = l - MI * 4;
+            lds_load16(d.b, stage(set) + 256 * j, voff_b[j]);
         } else {
             const int q = l - MI * 4;
             const int u = q / (4 * MI), e = (q / MI) % 4, nj = q % MI;
-            rb[S][nj][u][e] = __builtin_amdgcn_raw_buffer_load_b32(
+            rbr[S][nj][u][e] = __builtin_amdgcn_raw_buffer_load_b32(
                 d.b, ((8 * u + 4 * g + e) * ldb + nj * 32 + li) * 4, 0, 0);
         }
     };
@@ -743,7 +865,7 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
 #pragma unroll
         for (int l = 0; l < NL; ++l) load_one(d, l, set);
     };
-    // One block from set S, with block kb + D - 1's loads (into the set the
+    // One block from stage S, with block kb + D - 1's loads (into the stage the
     // previous block emptied) spread over its matrix instructions.
     auto step = [&](int kb, auto set) {
         constexpr int S = decltype(set)::value;
@@ -757,23 +879,72 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
                 for (int mi = 0; mi < MI; ++mi)
                     ra[S][mi][u] = mask_tail32(ra[S][mi][u], K - (k0 + 8 * u + 4 * g));
         }
+        // B's values of this lane: [nj][unit][e] = k-row 8u + 4g + e, column nj * 32 + li.
+        uint32_t rb[MI][4][4];
+        if constexpr (BL) {
+            read_b_frags64<(D - 2) * NL>(lds_addr((const char*)(stage(set) + 4 * g * TS + li)), rb);
+        } else {
+#pragma unroll
+            for (int nj = 0; nj < MI; ++nj)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rb[nj][u][e] = rbr[S][nj][u][e];
+        }
         if constexpr (!IL) {
 #pragma unroll
             for (int l = 0; l < NL; ++l) load_one(nd, l, SN{});
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (X3) {
+            // [half][block] hi and lo parts; split c (0 .. 2 MI - 1) of a half
+            // is A's block c when c < MI, else B's block c - MI.
+            u32x4 hi[2][2][MI], lo[2][2][MI];
+            auto split = [&](int h, int c) {
+                if (c < MI) {
+                    split8(ra[S][c][2 * h], ra[S][c][2 * h + 1], hi[h][0][c], lo[h][0][c]);
+                } else {
+                    const int nj = c - MI;
+                    const u32x4 x = {rb[nj][2 * h][0], rb[nj][2 * h][1], rb[nj][2 * h][2],
+                                     rb[nj][2 * h][3]};
+                    const u32x4 y = {rb[nj][2 * h + 1][0], rb[nj][2 * h + 1][1],
+                                     rb[nj][2 * h + 1][2], rb[nj][2 * h + 1][3]};
+                    split8(x, y, hi[h][1][nj], lo[h][1][nj]);
+                }
+            };
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            const int u = i / (4 * MI * MI), e = (i / (MI * MI)) % 4;
-            const int mi = (i / MI) % MI, nj = i % MI;
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                as_float(ra[S][mi][u][e]), as_float(rb[S][nj][u][e]), acc[mi][nj], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (IL) {
+            for (int c = 0; c < 2 * MI; ++c) split(0, c);
 #pragma unroll
-                for (int l = (i * NL) / NM; l < ((i + 1) * NL) / NM; ++l) load_one(nd, l, SN{});
+            for (int i = 0; i < NM; ++i) {
+                const int h = i / (3 * MI * MI), blk = (i / 3) % (MI * MI), t = i % 3;
+                const int mi = blk / MI, nj = blk % MI;
+                const u32x4 av = t == 0 ? lo[h][0][mi] : hi[h][0][mi];
+                const u32x4 bv = t == 1 ? lo[h][1][nj] : hi[h][1][nj];
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc[mi][nj], 0,
+                    0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (h == 0 && i < 2 * MI) split(1, i);
+                if constexpr (IL) {
+#pragma unroll
+                    for (int l = (i * NL) / NM; l < ((i + 1) * NL) / NM; ++l) load_one(nd, l, SN{});
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                const int u = i / (4 * MI * MI), e = (i / (MI * MI)) % 4;
+                const int mi = (i / MI) % MI, nj = i % MI;
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    as_float(ra[S][mi][u][e]), as_float(rb[nj][u][e]), acc[mi][nj], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (IL) {
+#pragma unroll
+                    for (int l = (i * NL) / NM; l < ((i + 1) * NL) / NM; ++l) load_one(nd, l, SN{});
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -806,20 +977,19 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
     // the end of C, so rows past M fall outside it, and columns past N get an
     // offset outside any range (the common epilogue's scheme).
     constexpr int PER = NB * 16 / W;
-    __shared__ float red[W][NB * 16][64];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave][b * 16 + r][lane] = acc[b / MI][b % MI][r];
+        for (int r = 0; r < 16; ++r) red[(wave * NB * 16 + b * 16 + r) * 64 + lane] = acc[b / MI][b % MI][r];
     __syncthreads();
     const __amdgpu_buffer_rsrc_t cr = c_rsrc(C, M, N, ldc, m0, n0, 4);
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int idx = wave * PER + q;
         const int b = idx / 16, r = idx % 16;
-        float v = red[0][idx][lane];
+        float v = red[idx * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += red[w][idx][lane];
+        for (int w = 1; w < W; ++w) v += red[(w * NB * 16 + idx) * 64 + lane];
         const int cl = (b % MI) * 32 + li;   // column within the tile
         const uint32_t off =
             (n0 + cl < N ? (uint32_t)((4 * g * ldc + cl) * 4) : OOB_LANE) +
@@ -846,10 +1016,10 @@ hipError_t go(const void* fn, const GemmLaunch& L) {
 }
 
 // Slice-K launches: one workgroup of W waves per TS x TS tile.
-template <int MI, int W, bool IL>
+template <int MI, int W, bool IL, bool X3>
 hipError_t go_slicek(const GemmLaunch& L) {
-    const void* fn = L.epi ? (const void*)gemm32_slicek_kernel<true, MI, W, IL>
-                           : (const void*)gemm32_slicek_kernel<false, MI, W, IL>;
+    const void* fn = L.epi ? (const void*)gemm32_slicek_kernel<true, MI, W, IL, X3>
+                           : (const void*)gemm32_slicek_kernel<false, MI, W, IL, X3>;
     const char* a = L.A;
     const char* b = L.B;
     char* c = L.C;
@@ -865,11 +1035,17 @@ hipError_t go_slicek(const GemmLaunch& L) {
 hipError_t launch_gemm32(const GemmLaunch& L) {
     if (L.out != OUT_F32 || L.tbm != L.tbn) return hipErrorInvalidValue;
     if (L.in == IN_F32 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 4)
-        return go_slicek<1, 4, true>(L);
+        return go_slicek<1, 4, true, false>(L);
     if (L.in == IN_F32 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 8)
-        return go_slicek<1, 8, false>(L);
+        return go_slicek<1, 8, false, false>(L);
     if (L.in == IN_F32 && L.splits == 1 && L.tbm == 64 && L.slice_waves == 4)
-        return go_slicek<2, 4, true>(L);
+        return go_slicek<2, 4, true, false>(L);
+    if (L.in == IN_F32X3 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 4)
+        return go_slicek<1, 4, true, true>(L);
+    if (L.in == IN_F32X3 && L.splits == 1 && L.tbm == 32 && L.slice_waves == 8)
+        return go_slicek<1, 8, false, true>(L);
+    if (L.in == IN_F32X3 && L.splits == 1 && L.tbm == 64 && L.slice_waves == 4)
+        return go_slicek<2, 4, true, true>(L);
     if (L.in == IN_F32 && L.tbm == 128)
         return go(L.epi ? (const void*)gemm32_kernel<true, 128> : (const void*)gemm32_kernel<false, 128>,
                   L);

@@ -214,13 +214,18 @@ def test_tile_map_rejects_bad_arguments():
     (4000, 3000, "f32", (128, 128)),      # 768 tiles (3 waves) beat 192 of 256^2
     (4096, 4096, "f32", (128, 128)),      # fp32 prefers 128^2 (two workgroups per CU)
     (2048, 2048, "f32", (128, 128)),      # 256 tiles of 128^2
-    (1024, 1152, "f32", (128, 128)),      # 72 tiles of 128^2: past the slice-K limit of 64
+    (2048, 1280, "f32", (128, 128)),      # 160 tiles of 128^2: past the fp32 slice-K limit of 144
+    (1536, 1536, "f32", (32, 32)),        # 144 tiles of 128^2: slice-K
+    (1024, 1152, "f32", (32, 32)),        # 72 tiles of 128^2: slice-K
     (1024, 1024, "f32", (64, 64)),        # 64 tiles of 128^2: slice-K, 256 tiles of 64^2
     (768, 768, "f32", (32, 32)),          # slice-K: 576 tiles of 32^2 share CUs three at a time
     (512, 512, "f32", (32, 32)),          # slice-K: 256 tiles of 32^2
     (1, 1, "f32", (32, 32)),
     (4000, 3000, "f32x3", (256, 256)),
-    (512, 512, "f32x3", (128, 128)),
+    (1024, 1152, "f32x3", (128, 128)),    # 72 tiles of 128^2: past the 3 x bf16 slice-K limit of 64
+    (1024, 1024, "f32x3", (64, 64)),      # slice-K, 256 tiles of 64^2
+    (768, 768, "f32x3", (64, 64)),
+    (512, 512, "f32x3", (32, 32)),        # slice-K: 256 tiles of 32^2
 ])
 def test_tile_choice(M, N, fmt, tile):
     info = dg.dgemm_tile_map(M, N, fmt)
@@ -254,7 +259,7 @@ def test_gemm_ex_validation_errors(in_fmt):
     assert call_ex(in_fmt, 0, 8, 8, 8, A=PA, lda=ld, B=PB, ldb=ld, C=PA, ldc=ld) == ALI
     # a workspace that a split plan would use, overlapping A (small fp32 outputs
     # take the slice-K kernel, which uses none)
-    M, N, K = (1024, 1024, 8192) if in_fmt == 0 else (64, 64, 1 << 14)
+    M, N, K = (1024, 1024, 16384) if in_fmt == 0 else (64, 64, 1 << 14)
     plan = dg.gemm_ex_plan({0: "f32", 1: "bf16", 2: "f16", 3: "f32x3"}[in_fmt], M, N, K, 1 << 30)
     assert plan["splits"] > 1
     assert call_ex(in_fmt, 0, M, N, K, A=PA, lda=K, B=PB, ldb=N, C=PC, ldc=N,
@@ -290,7 +295,8 @@ def test_plan_without_workspace_is_the_plain_launch(M, N, K, fmt):
     (16384, 4096, 4096, "bf16", 1),
     (4000, 3000, 4104, "bf16", 1),
     (512, 4096, 4096, "bf16", None),    # one GPU's row share of the 4096^3 problem
-    (1024, 1024, 8192, "f32", None),    # deep K: 8 splits of 128^2 beat slice-K
+    (1024, 1024, 16384, "f32", None),   # deep K: 8 splits of 128^2 beat slice-K
+    (256, 256, 8192, "f32x3", None),    # deep K: 16 splits of 128^2 beat slice-K
     (64, 64, 4096, "f16", None),
     (256, 256, 65536, "bf16", None),
 ])
@@ -322,12 +328,13 @@ from hypothesis import given, settings, strategies as st  # noqa: E402
 def test_plan_invariants(M, N, K, fmt, ws):
     p = dg.gemm_ex_plan(fmt, M, N, K, ws)
     tiles = {"f32": {(128, 128), (64, 64), (32, 32)}, "bf16": {(256, 256), (192, 256), (128, 128)},
-             "f16": {(256, 256), (192, 256), (128, 128)}, "f32x3": {(256, 256), (128, 128)}}[fmt]
+             "f16": {(256, 256), (192, 256), (128, 128)},
+             "f32x3": {(256, 256), (128, 128), (64, 64), (32, 32)}}[fmt]
     assert (p["tile_rows"], p["tile_cols"]) in tiles
     assert p["workspace_bytes"] <= ws
     if p["tile_rows"] < 128:
-        # slice-K: fp32 outputs of at most 64 tiles of 128^2, no workspace
-        assert fmt == "f32" and -(-M // 128) * -(-N // 128) <= 64
+        # slice-K: fp32 outputs of at most 144 tiles of 128^2 (3 x bf16: 64), no workspace
+        assert -(-M // 128) * -(-N // 128) <= {"f32": 144, "f32x3": 64}[fmt]
         assert p["splits"] == 1 and p["workspace_bytes"] == 0
     if p["stream_k"]:
         # one persistent workgroup per CU; two fp32 tiles and a flag each
@@ -374,36 +381,39 @@ def test_header_is_plain_c_and_the_c_client_links():
 
 
 def test_slice_k_plans_and_their_override():
-    """fp32 outputs of at most 64 tiles of 128^2 get the slice-K tiles (K split
-    across the waves of a workgroup): no workspace, whatever is offered, unless
-    a split plan is estimated clearly faster.  The plan override forces a
-    slice-K tile with its wave count in place of the split count."""
-    for M, N, K in [(512, 512, 512), (256, 256, 4096), (1024, 1024, 1024), (37, 65, 7), (8, 8, 0)]:
-        for ws in (0, 1 << 30):
-            p = dg.gemm_ex_plan("f32", M, N, K, ws)
-            t = dg.dgemm_tile_map(M, N, "f32")
-            assert p["tile_rows"] in (32, 64) and p["splits"] == 1 and p["workspace_bytes"] == 0
-            assert (p["tile_rows"], p["tile_cols"]) == (t["tile_rows"], t["tile_cols"])
-    # not for the other formats
-    assert dg.gemm_ex_plan("f32x3", 512, 512, 512, 0)["tile_rows"] == 128
+    """Small fp32 and 3 x bf16 outputs get the slice-K tiles (K split across the
+    waves of a workgroup): no workspace, whatever is offered, unless a split
+    plan is estimated clearly faster.  The plan override forces a slice-K tile
+    with its wave count in place of the split count."""
+    for fmt in ("f32", "f32x3"):
+        for M, N, K in [(512, 512, 512), (256, 256, 2048), (1024, 1024, 1024), (37, 65, 7),
+                        (8, 8, 0)]:
+            for ws in (0, 1 << 30):
+                p = dg.gemm_ex_plan(fmt, M, N, K, ws)
+                t = dg.dgemm_tile_map(M, N, fmt)
+                assert p["tile_rows"] in (32, 64) and p["splits"] == 1 and p["workspace_bytes"] == 0
+                assert (p["tile_rows"], p["tile_cols"]) == (t["tile_rows"], t["tile_cols"])
+    # not for the 16-bit formats
     assert dg.gemm_ex_plan("bf16", 512, 512, 512, 0)["tile_rows"] == 128
     try:
-        for tile, waves in ((32, 4), (32, 8), (64, 4), (32, 1), (64, 1)):
-            dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
-            p = dg.gemm_ex_plan("f32", 2000, 1500, 300, 1 << 30)  # beyond the automatic limit
-            assert (p["tile_rows"], p["tile_cols"], p["splits"], p["workspace_bytes"]) == \
-                (tile, tile, 1, 0)
-        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
-        auto = dg.gemm_ex_plan("f32", 2000, 1500, 300, 0)
-        assert auto["tile_rows"] == 128
-        for tile, waves in ((64, 8), (32, 3), (32, 2)):       # no such kernel: the planner's plan
-            dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
-            assert dg.gemm_ex_plan("f32", 2000, 1500, 300, 0) == auto
+        for fmt in ("f32", "f32x3"):
+            for tile, waves in ((32, 4), (32, 8), (64, 4), (32, 1), (64, 1)):
+                dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
+                p = dg.gemm_ex_plan(fmt, 2000, 1500, 300, 1 << 30)  # beyond the automatic limit
+                assert (p["tile_rows"], p["tile_cols"], p["splits"], p["workspace_bytes"]) == \
+                    (tile, tile, 1, 0)
+            dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+            auto = dg.gemm_ex_plan(fmt, 2000, 1500, 300, 0)
+            assert auto["tile_rows"] in (128, 256)
+            for tile, waves in ((64, 8), (32, 3), (32, 2)):    # no such kernel: the planner's plan
+                dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
+                assert dg.gemm_ex_plan(fmt, 2000, 1500, 300, 0) == auto
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 32, 32, 4)
-        assert dg.gemm_ex_plan("bf16", 512, 512, 512, 0)["tile_rows"] == 128  # fp32 only
-        # the 128 x 128 split plan stays reachable for small fp32 outputs
+        assert dg.gemm_ex_plan("bf16", 512, 512, 512, 0)["tile_rows"] == 128  # fp32 inputs only
+        # the 128 x 128 split plan stays reachable for small outputs
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 128, 128, 8)
-        p = dg.gemm_ex_plan("f32", 512, 512, 512, 1 << 30)
-        assert (p["tile_rows"], p["splits"]) == (128, 8)
+        for fmt in ("f32", "f32x3"):
+            p = dg.gemm_ex_plan(fmt, 512, 512, 512, 1 << 30)
+            assert (p["tile_rows"], p["splits"]) == (128, 8)
     finally:
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)

@@ -112,14 +112,14 @@ def test_k_zero_applies_the_epilogue_to_the_empty_sum(path, out):
     assert oracle.check(to64(C), E, np.zeros((M, N)), TOL_MFMA, out, b=b)["ok"]
 
 
-# Shapes whose best plan splits K, with the workspace it asks for.  fp32
-# outputs this small take the slice-K kernel instead, so the fp32 case forces
-# the split plan (128 x 128 tiles, 8 splits) through the plan override, which
-# the module's fixture clears after each test.
+# Shapes whose best plan splits K, with the workspace it asks for.  fp32 and
+# 3 x bf16 outputs this small take the slice-K kernel instead, so those cases
+# force the split plan (128 x 128 tiles, 8 splits) through the plan override,
+# which the module's fixture clears after each test.
 SPLIT_CASES = [("f32", "f32", 512, 512, 512), ("f32x3", "f32", 512, 512, 512),
                ("bf16", "f32", 64, 64, 4096), ("bf16", "bf16", 200, 136, 3000),
                ("f16", "f16", 64, 72, 4104), ("f16", "f32", 256, 256, 16384)]
-FORCED_SPLITS = {("f32", 512, 512, 512): (128, 128, 8)}
+FORCED_SPLITS = {("f32", 512, 512, 512): (128, 128, 8), ("f32x3", 512, 512, 512): (128, 128, 8)}
 
 
 def split_plan(path, out, M, N, K):

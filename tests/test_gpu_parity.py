@@ -95,7 +95,7 @@ def test_exact_integer_inputs_bitwise(path, out, M, N, K):
 
 # (workload, path, the macro-tile its plain launch uses).  Parametrizations of
 # one workload are adjacent so that the oracle's result is computed once.
-WORKLOAD_RUNS = [("f32_512", "f32", 32), ("f32_512", "f32x3", 128),
+WORKLOAD_RUNS = [("f32_512", "f32", 32), ("f32_512", "f32x3", 32),
                  ("f32_4096", "f32", 128), ("f32_4096", "f32x3", 256),
                  ("bf16_4096", "bf16", 256), ("f16_4096", "f16", 256),
                  ("bf16_16384x4096x4096", "bf16", 256), ("bf16_4000x3000x4104", "bf16", 192)]
@@ -215,8 +215,9 @@ def test_3xbf16_128_tile_step_counts(K):
     alternating by step, with each step loading three steps ahead and the K loop
     unrolled by two.  K from 1 to 200 gives 1 to 7 steps of 32, even and odd
     counts, with the ragged last step in either set.  Integer inputs (lo parts
-    zero): C is exact and must equal the oracle bit for bit."""
-    M, N = 300, 264
+    zero): C is exact and must equal the oracle bit for bit.  1100 x 1000 is 72
+    tiles of 128 x 128, past the outputs that take slice-K."""
+    M, N = 1100, 1000
     tm = dg.dgemm_tile_map(M, N, "f32x3")
     assert tm["tile_rows"] == 128
     print(f"case x3-128 K={K}", flush=True)

@@ -52,9 +52,9 @@ SEQUENCES = [
 ]
 
 
-# fp32 outputs this small take the slice-K kernel (no scratch): the fp32 call
-# forces the split plan through the plan override.
-FORCED_SPLITS = {("f32", 512, 512, 512): (128, 128, 8)}
+# fp32 and 3 x bf16 outputs this small take the slice-K kernel (no scratch):
+# those calls force the split plan through the plan override.
+FORCED_SPLITS = {("f32", 512, 512, 512): (128, 128, 8), ("f32x3", 512, 512, 512): (128, 128, 8)}
 
 
 @pytest.fixture
