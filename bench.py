@@ -539,16 +539,19 @@ def plan_compare(dg, args):
     return out
 
 
-# fp32 outputs of at most 64 tiles of 128 x 128: the cost model's slice-K plan
-# against the 128 x 128 grid kernel forced unsplit and split (the split count
-# the best of a sweep of 2-16 splits).
-F32_PLAN_SHAPES = [("f32 512^3 (the fp32 512^3 workload's shape)", 512, 512, 512, 8),
-                   ("f32 768^3", 768, 768, 768, 6),
-                   ("f32 1024^3", 1024, 1024, 1024, 4),
-                   ("f32 256x256x4096", 256, 256, 4096, 16)]
+# Small outputs of fp32 data (the fp32 and 3 x bf16 paths): the cost model's
+# slice-K plan against the 128 x 128 grid kernel forced unsplit and split (the
+# split count the best of a sweep of 2-16 splits).  (format, label, M, N, K, splits)
+SMALL_PLAN_SHAPES = [("f32", "f32 512^3 (the fp32 512^3 workload's shape)", 512, 512, 512, 8),
+                     ("f32", "f32 768^3", 768, 768, 768, 6),
+                     ("f32", "f32 1024^3", 1024, 1024, 1024, 4),
+                     ("f32", "f32 256x256x4096", 256, 256, 4096, 16),
+                     ("f32x3", "f32 via 3xbf16 512^3", 512, 512, 512, 4),
+                     ("f32x3", "f32 via 3xbf16 1024^3", 1024, 1024, 1024, 4),
+                     ("f32x3", "f32 via 3xbf16 512x512x4096", 512, 512, 4096, 16)]
 
 
-def plan_compare_f32(dg, args):
+def plan_compare_small(dg, args):
     """Per shape: gemm_ex timed by graph replay (these kernels take a few
     microseconds, less than the host's per-call cost) with the cost model's
     plan, and with the 128 x 128 grid kernel forced unsplit and split."""
@@ -556,23 +559,22 @@ def plan_compare_f32(dg, args):
     from synth_inputs import pair, to_torch
     out = []
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-
-    def ex_entry(a, b, c, stream=None):
-        dg.gemm_ex(a, b, c, workspace=ws, stream=stream)
     try:
-        for label, M, N, K, splits in F32_PLAN_SHAPES:
+        for fmt, label, M, N, K, splits in SMALL_PLAN_SHAPES:
+            def ex_entry(a, b, c, stream=None, fmt=fmt):
+                dg.gemm_ex(a, b, c, workspace=ws, in_fmt=fmt, stream=stream)
             A, B = pair(M, N, K, "uniform", "f32", seed=6100)
             Ad, Bd = to_torch(A, "f32").to("cuda"), to_torch(B, "f32").to("cuda")
             Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
-            print(f"bench: fp32 plans {label}", file=sys.stderr, flush=True)
-            rec = {"shape": label, "M": M, "N": N, "K": K}
+            print(f"bench: small-output plans {label}", file=sys.stderr, flush=True)
+            rec = {"shape": label, "format": fmt, "M": M, "N": N, "K": K}
             for key, force in (("cost_model", None), ("grid_128_unsplit", (128, 128, 1)),
                                ("grid_128_split", (128, 128, splits))):
                 if force:
                     dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, *force)
                 else:
                     dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
-                plan = dg.gemm_ex_plan("f32", M, N, K, ws.numel())
+                plan = dg.gemm_ex_plan(fmt, M, N, K, ws.numel())
                 for _ in range(20):
                     ex_entry(Ad, Bd, Cd)
                 torch.cuda.synchronize()
@@ -606,7 +608,7 @@ def main():
                          "so that timing starts from a settled clock (default 1.0)")
     ap.add_argument("--no-plans", action="store_true",
                     help="skip the cost model's plans against forced Stream-K (bf16) and forced "
-                         "128 x 128 grid plans (small fp32 outputs)")
+                         "128 x 128 grid plans (small outputs of fp32 data)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -714,7 +716,7 @@ def main():
         line["other_shapes"] = other_shapes(dg, args)
     if not args.no_plans:
         line["plan_compare"] = plan_compare(dg, args)
-        line["plan_compare_f32"] = plan_compare_f32(dg, args)
+        line["plan_compare_small"] = plan_compare_small(dg, args)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)

@@ -82,8 +82,8 @@ typedef enum {
  * fp32 inputs, fp32 C.  gfx950 has no reduced-precision (xf32) matrix
  * instruction, so products use the full-fp32 matrix instruction
  * v_mfma_f32_32x32x2_f32: the sgemm tf32 page's workload (section 0, M = N =
- * K = 4096 fp32) without its tf32 input truncation.  Outputs of at most 64
- * tiles of 128 x 128 (e.g. 512 x 512) run slice-K: 32 x 32 or 64 x 64 tiles
+ * K = 4096 fp32) without its tf32 input truncation.  Outputs of at most 144
+ * tiles of 128 x 128 (e.g. 1536 x 1536) run slice-K: 32 x 32 or 64 x 64 tiles
  * whose K is split across the 4 or 8 waves of one workgroup and summed in LDS
  * in wave order, so small products fill the GPU with no workspace; results
  * are deterministic for a given shape.
@@ -106,6 +106,7 @@ int gemm_f32(int M, int N, int K,
  * Non-finite inputs: a NaN propagates as in gemm_f32, but an infinite x has
  * lo = inf - inf = NaN, so the outputs it reaches are NaN, not infinite (as
  * are those of finite inputs too large for bf16, |x| >= (2 - 2^-8) * 2^127).
+ * Outputs of at most 64 tiles of 128 x 128 run slice-K as in gemm_f32.
  * Arguments, layout, errors and execution as gemm_f32.
  */
 int gemm_f32_3xbf16(int M, int N, int K,
@@ -261,10 +262,11 @@ typedef enum {
  * DGEMM_PLAN_GRID forces the macro-tile tile_rows x tile_cols (a shape the
  * input format's kernel has: 256 x 256, 192 x 256 or 128 x 128 for 16-bit
  * inputs, 128 x 128 for fp32, 256 x 256 or 128 x 128 for 3 x bf16) and
- * `splits` K pieces (>= 1; reduced to the number of K steps); for fp32 it
- * also forces the slice-K tiles, 32 x 32 or 64 x 64 at any M and N, where
- * `splits` gives the waves per workgroup instead (4 or 8 for 32 x 32, 4 for
- * 64 x 64, 1 for the planner's count; a slice-K plan has no K pieces);
+ * `splits` K pieces (>= 1; reduced to the number of K steps); for fp32 and
+ * 3 x bf16 it also forces the slice-K tiles, 32 x 32 or 64 x 64 at any M and
+ * N, where `splits` gives the waves per workgroup instead (4 or 8 for
+ * 32 x 32, 4 for 64 x 64, 1 for the planner's count; a slice-K plan has no K
+ * pieces);
  * DGEMM_PLAN_STREAM_K forces a Stream-K plan, DGEMM_PLAN_NO_STREAM_K rules it
  * out (tile and split arguments ignored by both).  A forced plan the call cannot take (tile shape the kernel lacks,
  * workspace too small, Stream-K for fp32 inputs or under graph capture) falls
