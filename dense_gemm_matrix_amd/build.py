@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # the C ABI and planner, then one file per kernel family
-SOURCES = [os.path.join(CSRC, f) for f in ("dgemm.hip", "gemm16.hip", "gemm32.hip", "splitk.hip")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("dgemm.hip", "gemm16.hip", "gemm32.hip", "slicek16.hip", "splitk.hip")]
 LIB = os.path.join(PKG, "libdgemm.so")
 # The benchmark's matrix-instruction ceiling kernel: a library of its own,
 # loaded only by bench.py, never by the package.

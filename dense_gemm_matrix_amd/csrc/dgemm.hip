@@ -232,11 +232,21 @@ constexpr SliceCand SLICE_F32[] = {{32, 4, 2.4, 0.9, 0.82, 0.1},
 constexpr SliceCand SLICE_X3[] = {{32, 4, 2.4, 0.72, 0.86, 0.1},
                                   {32, 8, 2.5, 1.19, 1.0, 1.6},
                                   {64, 4, 3.6, 1.28, 1.04, 2.9}};
+// bf16 / fp16 (blocks of 64 k): the same tiles; 8 waves were never faster
+// than 4 in the sweep (the 64 x 64 tile's rounds are not fitted: at most 64
+// tiles of 128 x 128 give it one round).
+constexpr SliceCand SLICE_16[] = {{32, 4, 2.45, 0.60, 1.04, 0.6},
+                                  {32, 8, 2.45, 1.22, 1.08, 1.4},
+                                  {64, 4, 3.0, 1.14, 1.0, 2.9}};
 
-bool slice_format(int in) { return in == IN_F32 || in == IN_F32X3; }
+bool slice_format(int in) { (void)in; return true; }
+
+// K per slice-K block: 64 for 16-bit inputs, 32 for fp32 data.
+int slice_bk(int in) { return (in == IN_BF16 || in == IN_F16) ? 64 : 32; }
 
 const SliceCand* slice_cands(int in, int& n) {
     n = 3;
+    if (in == IN_BF16 || in == IN_F16) return SLICE_16;
     return in == IN_F32X3 ? SLICE_X3 : SLICE_F32;
 }
 
@@ -244,7 +254,9 @@ const SliceCand* slice_cands(int in, int& n) {
 // (1536^2; at 1024 x 2048 x 1024 44 against 67 us for the grid, at 1536^3 79
 // against 98 us; at 2048^2 x 1024 the grid is faster, 69 against 89 us); for
 // 3 x bf16, whose grid kernel is five times faster per tile, up to 64 (at 128
-// and 144 tiles the two were within 10 % either way).
+// and 144 tiles the two were within 10 % either way); for bf16 / fp16 up to
+// 64 (at 128 tiles the grid was faster, 11.8 against 14.8 us at
+// 1024 x 2048 x 1024).
 int64_t slice_max_tiles128(int in) { return in == IN_F32 ? 144 : 64; }
 
 bool slice_eligible(int in, int M, int N) {
@@ -258,9 +270,9 @@ int64_t slice_per_cu(const SliceCand& c, int M, int N) {
 
 double slice_load(const SliceCand& c, int64_t n) { return n == 1 ? 1.0 : (double)n * c.co; }
 
-double estimate_slice_us(const SliceCand& c, int M, int N, int K) {
+double estimate_slice_us(int in, const SliceCand& c, int M, int N, int K) {
     const int64_t n = slice_per_cu(c, M, N);
-    const int64_t nbw = ceil_div(ceil_div(K, 32), c.waves);
+    const int64_t nbw = ceil_div(ceil_div(K, slice_bk(in)), c.waves);
     return c.fixed_us + (double)nbw * c.blk_us * slice_load(c, n) + (double)(n - 1) * c.round_us;
 }
 
@@ -294,7 +306,7 @@ int slice_waves(int in, int ts, int M, int N, int K) {
     double best_us = 0.0;
     for (int i = 0; i < n; ++i) {
         if (c[i].ts != ts) continue;
-        const double us = estimate_slice_us(c[i], M, N, K);
+        const double us = estimate_slice_us(in, c[i], M, N, K);
         if (best == 0 || us < best_us) { best = c[i].waves; best_us = us; }
     }
     return best;
@@ -414,7 +426,7 @@ Plan make_plan_auto(int in, int es_out, int M, int N, int K, uint64_t ws_avail, 
     const int bk = bk_of(in);
     const int nk = (int)ceil_div(K, bk);
     const int ldw = (int)ceil_div(N, 4) * 4;
-    double best = (slice ? estimate_slice_us(*slice_cand(in, plan.bm, plan.waves), M, N, K)
+    double best = (slice ? estimate_slice_us(in, *slice_cand(in, plan.bm, plan.waves), M, N, K)
                          : estimate_us(in, es_out, M, N, base, 1, nk, ldw)) *
                   SPLIT_MARGIN;
     int ncand = 0;
@@ -525,7 +537,9 @@ bool epi_needed(const EpiArgs& e) {
 }
 
 hipError_t launch_family(const GemmLaunch& L) {
-    return (L.in == IN_BF16 || L.in == IN_F16) ? launch_gemm16(L) : launch_gemm32(L);
+    if (L.in == IN_BF16 || L.in == IN_F16)
+        return L.slice_waves > 0 ? launch_slicek16(L) : launch_gemm16(L);
+    return launch_gemm32(L);
 }
 
 // Validated arguments and a plan -> one GEMM launch, a split GEMM into the

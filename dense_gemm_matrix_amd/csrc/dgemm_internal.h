@@ -58,7 +58,7 @@ struct EpiArgs {
 struct GemmLaunch {
     int in, out, tbm, tbn;
     int stages;  // LDS stages of the 16-bit kernel's 128 x 128 tile (2, or 4 alone on a CU)
-    int slice_waves;  // waves per workgroup of the fp32 slice-K kernel
+    int slice_waves;  // waves per workgroup of a slice-K launch (0: a grid launch)
     bool epi;    // apply `e` in the kernel (only with splits == 1)
     const char* A;
     const char* B;
@@ -182,6 +182,7 @@ hipError_t launch_gemm16(const GemmLaunch& L);  // IN_BF16, IN_F16
 // splits = 1; `grid` workgroups, a multiple of NUM_XCD.
 hipError_t launch_gemm16_sk(const GemmLaunch& L, const SkSched& s, int grid);
 hipError_t launch_gemm32(const GemmLaunch& L);  // IN_F32, IN_F32X3
+hipError_t launch_slicek16(const GemmLaunch& L);  // IN_BF16, IN_F16 with slice_waves > 0
 
 // Split-K reduction: C[i][j] = epilogue(sum_{z < splits} W[z][i][j]) with W
 // fp32, row pitch ldw (a multiple of 4) and split stride zstride elements.

@@ -209,7 +209,9 @@ def test_tile_map_rejects_bad_arguments():
     (16384, 4096, "bf16", (256, 256)),    # four full waves of tiles
     (4000, 3000, "bf16", (192, 256)),     # 252 tiles instead of 192
     (4000, 3000, "f16", (192, 256)),
-    (512, 512, "bf16", (128, 128)),       # 16 tiles instead of 4
+    (512, 512, "bf16", (32, 32)),         # slice-K: 256 tiles of 32^2
+    (1024, 1024, "f16", (64, 64)),        # slice-K: 256 tiles of 64^2
+    (1024, 1152, "bf16", (128, 128)),     # 72 tiles of 128^2: past the 16-bit slice-K limit of 64
     (2048, 2048, "f16", (128, 128)),      # 256 tiles instead of 64
     (4000, 3000, "f32", (128, 128)),      # 768 tiles (3 waves) beat 192 of 256^2
     (4096, 4096, "f32", (128, 128)),      # fp32 prefers 128^2 (two workgroups per CU)
@@ -327,14 +329,15 @@ from hypothesis import given, settings, strategies as st  # noqa: E402
        ws=st.sampled_from([0, 1, 1 << 16, 1 << 20, 1 << 24, 1 << 28, 1 << 40]))
 def test_plan_invariants(M, N, K, fmt, ws):
     p = dg.gemm_ex_plan(fmt, M, N, K, ws)
-    tiles = {"f32": {(128, 128), (64, 64), (32, 32)}, "bf16": {(256, 256), (192, 256), (128, 128)},
-             "f16": {(256, 256), (192, 256), (128, 128)},
-             "f32x3": {(256, 256), (128, 128), (64, 64), (32, 32)}}[fmt]
+    slice = {(64, 64), (32, 32)}
+    tiles = {"f32": {(128, 128)} | slice, "bf16": {(256, 256), (192, 256), (128, 128)} | slice,
+             "f16": {(256, 256), (192, 256), (128, 128)} | slice,
+             "f32x3": {(256, 256), (128, 128)} | slice}[fmt]
     assert (p["tile_rows"], p["tile_cols"]) in tiles
     assert p["workspace_bytes"] <= ws
     if p["tile_rows"] < 128:
-        # slice-K: fp32 outputs of at most 144 tiles of 128^2 (3 x bf16: 64), no workspace
-        assert -(-M // 128) * -(-N // 128) <= {"f32": 144, "f32x3": 64}[fmt]
+        # slice-K: outputs of at most 144 tiles of 128^2 (fp32) or 64 (the others), no workspace
+        assert -(-M // 128) * -(-N // 128) <= (144 if fmt == "f32" else 64)
         assert p["splits"] == 1 and p["workspace_bytes"] == 0
     if p["stream_k"]:
         # one persistent workgroup per CU; two fp32 tiles and a flag each
@@ -381,11 +384,11 @@ def test_header_is_plain_c_and_the_c_client_links():
 
 
 def test_slice_k_plans_and_their_override():
-    """Small fp32 and 3 x bf16 outputs get the slice-K tiles (K split across the
-    waves of a workgroup): no workspace, whatever is offered, unless a split
-    plan is estimated clearly faster.  The plan override forces a slice-K tile
-    with its wave count in place of the split count."""
-    for fmt in ("f32", "f32x3"):
+    """Small outputs get the slice-K tiles (K split across the waves of a
+    workgroup), in every input format: no workspace, whatever is offered,
+    unless a split plan is estimated clearly faster.  The plan override forces
+    a slice-K tile with its wave count in place of the split count."""
+    for fmt in ("f32", "f32x3", "bf16", "f16"):
         for M, N, K in [(512, 512, 512), (256, 256, 2048), (1024, 1024, 1024), (37, 65, 7),
                         (8, 8, 0)]:
             for ws in (0, 1 << 30):
@@ -393,10 +396,8 @@ def test_slice_k_plans_and_their_override():
                 t = dg.dgemm_tile_map(M, N, fmt)
                 assert p["tile_rows"] in (32, 64) and p["splits"] == 1 and p["workspace_bytes"] == 0
                 assert (p["tile_rows"], p["tile_cols"]) == (t["tile_rows"], t["tile_cols"])
-    # not for the 16-bit formats
-    assert dg.gemm_ex_plan("bf16", 512, 512, 512, 0)["tile_rows"] == 128
     try:
-        for fmt in ("f32", "f32x3"):
+        for fmt in ("f32", "f32x3", "bf16", "f16"):
             for tile, waves in ((32, 4), (32, 8), (64, 4), (32, 1), (64, 1)):
                 dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
                 p = dg.gemm_ex_plan(fmt, 2000, 1500, 300, 1 << 30)  # beyond the automatic limit
@@ -404,15 +405,13 @@ def test_slice_k_plans_and_their_override():
                     (tile, tile, 1, 0)
             dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
             auto = dg.gemm_ex_plan(fmt, 2000, 1500, 300, 0)
-            assert auto["tile_rows"] in (128, 256)
+            assert auto["tile_rows"] in (128, 192, 256)
             for tile, waves in ((64, 8), (32, 3), (32, 2)):    # no such kernel: the planner's plan
                 dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, tile, tile, waves)
                 assert dg.gemm_ex_plan(fmt, 2000, 1500, 300, 0) == auto
-        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 32, 32, 4)
-        assert dg.gemm_ex_plan("bf16", 512, 512, 512, 0)["tile_rows"] == 128  # fp32 inputs only
-        # the 128 x 128 split plan stays reachable for small outputs
+        # the 128 x 128 grid, split or not, stays reachable for small outputs
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 128, 128, 8)
-        for fmt in ("f32", "f32x3"):
+        for fmt in ("f32", "f32x3", "bf16", "f16"):
             p = dg.gemm_ex_plan(fmt, 512, 512, 512, 1 << 30)
             assert (p["tile_rows"], p["splits"]) == (128, 8)
     finally:

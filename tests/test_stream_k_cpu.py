@@ -181,7 +181,7 @@ def test_plan_override_and_the_plan_query():
         # a tile shape the kernel does not have: the cost model's plan
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
         auto = dg.gemm_ex_plan("bf16", 4000, 3000, 4104, ws)
-        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 64, 64, 1)
+        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 96, 96, 1)
         assert dg.gemm_ex_plan("bf16", 4000, 3000, 4104, ws) == auto
         # Stream-K ruled out
         dg.dgemm_set_plan_override(dg.DGEMM_PLAN_NO_STREAM_K)
