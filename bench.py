@@ -539,16 +539,20 @@ def plan_compare(dg, args):
     return out
 
 
-# Small outputs of fp32 data (the fp32 and 3 x bf16 paths): the cost model's
-# slice-K plan against the 128 x 128 grid kernel forced unsplit and split (the
-# split count the best of a sweep of 2-16 splits).  (format, label, M, N, K, splits)
+# Small outputs, every input format: the cost model's slice-K plan against the
+# 128 x 128 grid kernel forced unsplit and split (the split count the best of
+# a sweep of 2-16 splits); fp32 C.  (format, label, M, N, K, splits)
 SMALL_PLAN_SHAPES = [("f32", "f32 512^3 (the fp32 512^3 workload's shape)", 512, 512, 512, 8),
                      ("f32", "f32 768^3", 768, 768, 768, 6),
                      ("f32", "f32 1024^3", 1024, 1024, 1024, 4),
                      ("f32", "f32 256x256x4096", 256, 256, 4096, 16),
                      ("f32x3", "f32 via 3xbf16 512^3", 512, 512, 512, 4),
                      ("f32x3", "f32 via 3xbf16 1024^3", 1024, 1024, 1024, 4),
-                     ("f32x3", "f32 via 3xbf16 512x512x4096", 512, 512, 4096, 16)]
+                     ("f32x3", "f32 via 3xbf16 512x512x4096", 512, 512, 4096, 16),
+                     ("bf16", "bf16 512^3", 512, 512, 512, 2),
+                     ("bf16", "bf16 1024^3", 1024, 1024, 1024, 2),
+                     ("bf16", "bf16 512x512x4096", 512, 512, 4096, 8),
+                     ("bf16", "bf16 256x256x8192", 256, 256, 8192, 16)]
 
 
 def plan_compare_small(dg, args):
@@ -563,8 +567,9 @@ def plan_compare_small(dg, args):
         for fmt, label, M, N, K, splits in SMALL_PLAN_SHAPES:
             def ex_entry(a, b, c, stream=None, fmt=fmt):
                 dg.gemm_ex(a, b, c, workspace=ws, in_fmt=fmt, stream=stream)
-            A, B = pair(M, N, K, "uniform", "f32", seed=6100)
-            Ad, Bd = to_torch(A, "f32").to("cuda"), to_torch(B, "f32").to("cuda")
+            dt = "f32" if fmt == "f32x3" else fmt
+            A, B = pair(M, N, K, "uniform", dt, seed=6100)
+            Ad, Bd = to_torch(A, dt).to("cuda"), to_torch(B, dt).to("cuda")
             Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
             print(f"bench: small-output plans {label}", file=sys.stderr, flush=True)
             rec = {"shape": label, "format": fmt, "M": M, "N": N, "K": K}
@@ -608,7 +613,7 @@ def main():
                          "so that timing starts from a settled clock (default 1.0)")
     ap.add_argument("--no-plans", action="store_true",
                     help="skip the cost model's plans against forced Stream-K (bf16) and forced "
-                         "128 x 128 grid plans (small outputs of fp32 data)")
+                         "128 x 128 grid plans (small outputs)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 

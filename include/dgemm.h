@@ -118,7 +118,9 @@ int gemm_f32_3xbf16(int M, int N, int K,
 /*
  * bf16 inputs (raw 16-bit storage), fp32 accumulation, C fp32 (out =
  * DGEMM_OUT_F32) or bf16 (out = DGEMM_OUT_SAME).  The hgemm page's workload
- * (section 0, M = N = K = 4096, bf16 in and out).
+ * (section 0, M = N = K = 4096, bf16 in and out).  Outputs of at most 64
+ * tiles of 128 x 128 run slice-K as in gemm_f32 (K split across the waves of
+ * one workgroup, summed in LDS in wave order; no workspace).
  */
 int gemm_bf16(int M, int N, int K,
               const void* A, int lda,
@@ -262,11 +264,10 @@ typedef enum {
  * DGEMM_PLAN_GRID forces the macro-tile tile_rows x tile_cols (a shape the
  * input format's kernel has: 256 x 256, 192 x 256 or 128 x 128 for 16-bit
  * inputs, 128 x 128 for fp32, 256 x 256 or 128 x 128 for 3 x bf16) and
- * `splits` K pieces (>= 1; reduced to the number of K steps); for fp32 and
- * 3 x bf16 it also forces the slice-K tiles, 32 x 32 or 64 x 64 at any M and
- * N, where `splits` gives the waves per workgroup instead (4 or 8 for
- * 32 x 32, 4 for 64 x 64, 1 for the planner's count; a slice-K plan has no K
- * pieces);
+ * `splits` K pieces (>= 1; reduced to the number of K steps); it also forces
+ * the slice-K tiles, 32 x 32 or 64 x 64 at any M and N in every input format,
+ * where `splits` gives the waves per workgroup instead (4 or 8 for 32 x 32, 4
+ * for 64 x 64, 1 for the planner's count; a slice-K plan has no K pieces);
  * DGEMM_PLAN_STREAM_K forces a Stream-K plan, DGEMM_PLAN_NO_STREAM_K rules it
  * out (tile and split arguments ignored by both).  A forced plan the call cannot take (tile shape the kernel lacks,
  * workspace too small, Stream-K for fp32 inputs or under graph capture) falls
