@@ -975,7 +975,11 @@ __global__ __launch_bounds__(64 * W) void gemm32_slicek_kernel(
     // row 32 (b / MI) + 8 (r / 4) + 4 g + r % 4, column 32 (b % MI) + li of
     // the tile; stores go through a buffer resource from the tile's corner to
     // the end of C, so rows past M fall outside it, and columns past N get an
-    // offset outside any range (the common epilogue's scheme).
+    // offset outside any range (the common epilogue's scheme).  BL: the last
+    // blocks' direct-to-LDS loads (empty ranges past the run, which still write
+    // zeros into the stages) land first, so none is left in flight when the
+    // workgroup's LDS is released.
+    if constexpr (BL) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     constexpr int PER = NB * 16 / W;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
