@@ -357,13 +357,16 @@ def test_random_shapes_epilogues_and_plans(case):
 
 
 @pytest.mark.parametrize("path,out,M,N,K", [("bf16", "bf16", 64, 72, 4104), ("f16", "f32", 300, 264, 200),
-                                            ("f32", "f32", 512, 512, 512)])
+                                            ("f32", "f32", 512, 512, 512),
+                                            ("f32x3", "f32", 1024, 1024, 1024),
+                                            ("bf16", "f32", 1024, 1024, 1024)])
 def test_hip_graph_capture_replays_match_eager(path, out, M, N, K):
-    """gemm_ex (a split plan where the planner picks one; slice-K for fp32 512^3)
-    captured into a HIP
-    graph: every replay, with eager work on the same stream between replays,
-    reproduces the eager result bit for bit.  The library enqueues only kernel
-    launches (no memset, no allocation), which is what capture requires."""
+    """gemm_ex captured into a HIP graph, on the planner's plans: a split plan
+    (bf16 64 x 72 x 4104) and slice-K on 32 x 32 and 64 x 64 tiles (the others;
+    the 64 x 64 tiles move B through LDS with direct-to-LDS loads): every
+    replay, with eager work on the same stream between replays, reproduces the
+    eager result bit for bit.  The library enqueues only kernel launches (no
+    memset, no allocation), which is what capture requires."""
     p = dg.gemm_ex_plan(path, M, N, K, 1 << 40, out_same=(out != "f32"))
     print(f"case graph {path}->{out} {M}x{N}x{K} plan {p}", flush=True)
     rng = np.random.default_rng(6300 + M)
@@ -373,8 +376,9 @@ def test_hip_graph_capture_replays_match_eager(path, out, M, N, K):
     Ad, Bd = dev_matrix(A, dtype), dev_matrix(B, dtype)
     bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32)).to("cuda")
     ws = torch.empty(max(p["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
+    fmt = "f32x3" if path == "f32x3" else None
     ref = torch.empty((M, N), dtype=TORCH[out], device="cuda")
-    dg.gemm_ex(Ad, Bd, ref, bias=bias, relu=True, workspace=ws)
+    dg.gemm_ex(Ad, Bd, ref, bias=bias, relu=True, workspace=ws, in_fmt=fmt)
     torch.cuda.synchronize()
     C = torch.empty_like(ref)
     other = torch.empty_like(ref)
@@ -382,14 +386,14 @@ def test_hip_graph_capture_replays_match_eager(path, out, M, N, K):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws)   # warm-up outside capture
+        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws, in_fmt=fmt)  # warm-up outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws)
+        dg.gemm_ex(Ad, Bd, C, bias=bias, relu=True, workspace=ws, in_fmt=fmt)
     for rep in range(4):
         C.fill_(float("nan"))
         g.replay()
-        dg.gemm_ex(Ad, Bd, other, workspace=ws)                    # eager work between replays
+        dg.gemm_ex(Ad, Bd, other, workspace=ws, in_fmt=fmt)       # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(C, ref), rep
