@@ -161,3 +161,22 @@ def test_128_tile_ragged_edges_when_forced(fmt, M, N, K):
     C64, _ = oracle.gemm("f32", A, B)
     assert np.array_equal(to64(C), C64)
     assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("fmt,tile,waves", VARIANTS)
+def test_very_deep_k_all_ones(fmt, tile, waves):
+    """K = 2^20 + 37 (32769 blocks of 32 k, the last one ragged, shared among the
+    waves; NaN in A's row padding past K): with all-ones inputs every element of
+    C is exactly K (< 2^24, so exact in fp32; the bf16 lo parts are zero), a
+    closed form the oracle's definition gives at any size."""
+    force(fmt, tile, waves)
+    M, N, K = 96, 72, (1 << 20) + 37
+    print(f"case slicek {fmt} {tile}/{waves} all-ones K={K}", flush=True)
+    A = torch.full((M, round_pitch(K, "f32")), float("nan"), device="cuda")[:, :K]
+    A.fill_(1.0)  # NaN stays in the row padding past K
+    B = torch.ones((K, N), dtype=torch.float32, device="cuda")
+    C = sentinel_c(M, N, "f32")
+    dg.gemm_ex(A, B, C, in_fmt=fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(to64(C), np.full((M, N), float(K)))
+    assert gap_untouched(C)

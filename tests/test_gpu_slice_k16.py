@@ -145,3 +145,24 @@ def test_128_tile_ragged_edges_when_forced(fmt, out, M, N, K):
     C64, _ = oracle.gemm(fmt, A, B)
     assert np.array_equal(to64(C), expect_exact(out, C64))
     assert gap_untouched(C)
+
+
+@pytest.mark.parametrize("fmt,out,tile,waves", VARIANTS)
+def test_very_deep_k_all_ones(fmt, out, tile, waves):
+    """K = 2^20 + 37 (16385 blocks of 64 k, the last one ragged, shared among the
+    waves; NaN in A's row padding past K): with all-ones inputs every element of
+    C is exactly K (rounded once to 16-bit C), a closed form the oracle's
+    definition gives at any size."""
+    force(fmt, out, tile, waves)
+    M, N, K = 96, 72, (1 << 20) + 37
+    print(f"case slicek16 {fmt}->{out} {tile}/{waves} all-ones K={K}", flush=True)
+    dtype = {"bf16": torch.bfloat16, "f16": torch.float16}[fmt]
+    A = torch.full((M, round_pitch(K, fmt)), float("nan"), dtype=dtype, device="cuda")[:, :K]
+    A.fill_(1.0)  # NaN stays in the row padding past K
+    B = torch.ones((K, N), dtype=dtype, device="cuda")
+    C = sentinel_c(M, N, out)
+    dg.gemm_ex(A, B, C)
+    torch.cuda.synchronize()
+    expect = expect_exact(out, np.full((M, N), float(K)))
+    assert np.array_equal(to64(C), expect)
+    assert gap_untouched(C)
