@@ -65,8 +65,11 @@ def check(C, E, i0, j1, inf_column_exact=True):
     assert np.array_equal(C[rest], E[rest]), "finite outputs differ from the oracle"
 
 
+@pytest.mark.parametrize("grid128", [False, True])
 @pytest.mark.parametrize("path,out", COMBOS)
-def test_nan_row_and_infinite_column(path, out):
+def test_nan_row_and_infinite_column(path, out, grid128):
+    """Through the plain entry point (the planner's plan: slice-K at this size),
+    and through gemm_ex with the 128 x 128 grid kernel forced."""
     M, N, K = 200, 136, 300          # ragged in every dimension; k1 in the K tail step
     i0, k0, k1, j1 = 5, 17, 290, 130
     dtype = "f32" if path == "f32x3" else path
@@ -74,9 +77,18 @@ def test_nan_row_and_infinite_column(path, out):
     Ad = dev_matrix(to_storage(A, dtype), dtype)
     Bd = dev_matrix(to_storage(B, dtype), dtype)
     Cd = sentinel_c(M, N, out)
-    ENTRY[path](Ad, Bd, Cd)
+    if grid128:
+        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, 128, 128, 1)
+        try:
+            assert dg.gemm_ex_plan(path, M, N, K, 0, out_same=(out != "f32"))["tile_rows"] == 128
+            dg.gemm_ex(Ad, Bd, Cd, in_fmt="f32x3" if path == "f32x3" else None)
+        finally:
+            dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+    else:
+        assert dg.gemm_ex_plan(path, M, N, K, 0, out_same=(out != "f32"))["tile_rows"] == 32
+        ENTRY[path](Ad, Bd, Cd)
     torch.cuda.synchronize()
-    print(f"nonfinite {path}->{out} {M}x{N}x{K}", flush=True)
+    print(f"nonfinite {path}->{out} {M}x{N}x{K} grid128={grid128}", flush=True)
     check(to64(Cd), expected(dtype, out, A, A0, B0, i0, k1, j1), i0, j1,
           inf_column_exact=(path != "f32x3"))
     assert gap_untouched(Cd)
