@@ -153,7 +153,7 @@ typedef enum {
 
 /*
  * The general entry point: GEMM with a fused epilogue and an optional split-K
- * plan.
+ * plan (or slice-K, Stream-K; see below).
  *
  *     C[i][j] := act(alpha * sum_k A[i][k] * B[k][j] + beta * C[i][j] + bias[j])
  *
@@ -180,6 +180,14 @@ typedef enum {
  * workspace is scratch: its contents before and after the call are
  * unspecified, and calls that share one workspace must be ordered (same
  * stream).  gemm_ex_plan reports the plan and the bytes it uses.
+ *
+ * Slice-K: small outputs (at most 144 tiles of 128 x 128 for fp32, 64 for the
+ * other input formats) run by default on 32 x 32 or 64 x 64 tiles whose K is
+ * split across the waves of one workgroup and summed in LDS in wave order:
+ * no workspace and no second kernel, deterministic for a given shape.  Offered
+ * a workspace, the planner compares this plan with the split plans by their
+ * estimated times and takes a split plan only when it is estimated at least
+ * 10 % faster (deep K on few tiles).
  *
  * Stream-K (the nine-levels tutorial, section 2.9: the refinement of Split-K
  * that gives every thread block the same amount of work): for bf16 / fp16
