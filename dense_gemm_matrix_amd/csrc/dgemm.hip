@@ -125,7 +125,20 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // rounds = ceil(tiles * s / 256) workgroups per CU.  128 x 128 tiles fit two
 // workgroups on a CU: two co-resident ones take `pair` times as long as one
 // alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them rounds counts pairs and
-// the term in parentheses is multiplied by `pair`.  A grid of at most one
+// the term in parentheses is multiplied by `pair`.  For the 16-bit 256 x 256
+// and 192 x 256 tiles a last round that fills a fraction f of the CUs counts
+// `last + (1 - last) * f` of a full round (last = 0.6): under the power cap a
+// partly filled chip runs at a higher clock, so a grid of 1.25 rounds takes
+// ~1.7 times one round, not 2.  The rule picks the unsplit tile (`pick_tile`);
+// the split-K choice below keeps whole rounds, as in the sweeps it was fitted
+// to (with the rule there, two K = 16384 shapes dropped a 2-way split that is
+// 4-6 % faster).  bf16, 36 shapes from 2048 x 8192 to 8192^2 at K = 2048 and
+// 4096, unsplit: the fastest of the three tiles on 32 (14 before the rule chose
+// 128 x 128 tiles 6-11 % slower than the best; the 4 left, at 6144 x 4096 and
+// 8192 x 5120, were among them); on 7 more shapes whose tile it changes, 1-16 %
+// faster.  The 3 x bf16 256 x 256 tile keeps whole rounds: its second round
+// costs ~0.6 of the first whatever its fill, but its 128 x 128 tile wins anyway
+// on the shapes where a partial-round rule would pick the 256 x 256 one.  A grid of at most one
 // workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
 // runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU,
 // and the 3 x bf16 one is measured faster alone on its CU than its pair factor
@@ -150,16 +163,22 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 // sweep of forced plans 256 x 256 was slower at every shape (4096^3: 1049 us
 // against 1002 us), and the cost model never chose it; eff stays relative to
 // a 256 x 256 workgroup so that step_us keeps one meaning.
-struct TileCand { int bm, bn; double eff, pair, eff1; };
-constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 1.0}, {192, 256, 0.95, 0.0, 0.95},
-                                {128, 128, 0.6, 1.26, 0.8}};
-constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 0.85}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0}, {128, 128, 0.5, 1.22, 0.6}};
+// `last`: the cost of a last, partly filled round at zero fill (1: whole rounds).
+struct TileCand { int bm, bn; double eff, pair, eff1, last; };
+constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 1.0, 0.6}, {192, 256, 0.95, 0.0, 0.95, 0.6},
+                                {128, 128, 0.6, 1.26, 0.8, 1.0}};
+constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 0.85, 1.0}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0, 1.0}, {128, 128, 0.5, 1.22, 0.6, 1.0}};
 
-// Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round.
-double rounds_factor(const TileCand& t, int64_t wgs) {
+// Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round;
+// `partial`: price a partly filled last round by the tile's `last`.
+double rounds_factor(const TileCand& t, int64_t wgs, bool partial = false) {
     const int64_t per_cu = (wgs + NUM_CU - 1) / NUM_CU;
     if (t.pair > 0.0 && per_cu >= 2) return (double)((per_cu + 1) / 2) * t.pair;
+    if (partial && per_cu >= 2 && t.last < 1.0) {
+        const double fill = (double)(wgs - (per_cu - 1) * NUM_CU) / NUM_CU;
+        return (double)(per_cu - 1) + t.last + (1.0 - t.last) * fill;
+    }
     return (double)per_cu;
 }
 
@@ -325,7 +344,7 @@ Plan slice_plan(int in, int M, int N, int K) {
 TileCand pick_tile(int in, int M, int N) {
     if (slice_eligible(in, M, N)) {
         const int ts = slice_tile(in, M, N);
-        return TileCand{ts, ts, 1.0, 0.0, 1.0};
+        return TileCand{ts, ts, 1.0, 0.0, 1.0, 1.0};
     }
     int n = 0;
     const TileCand* cands = tiles_for(in, n);
@@ -334,7 +353,7 @@ TileCand pick_tile(int in, int M, int N) {
     for (int i = 0; i < n; ++i) {
         const TileCand& c = cands[i];
         const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-        const double cost = rounds_factor(c, tiles) * c.bm * c.bn / tile_eff(c, tiles);
+        const double cost = rounds_factor(c, tiles, true) * c.bm * c.bn / tile_eff(c, tiles);
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c; }
     }
     return best;

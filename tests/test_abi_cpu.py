@@ -209,6 +209,15 @@ def test_tile_map_rejects_bad_arguments():
     (16384, 4096, "bf16", (256, 256)),    # four full waves of tiles
     (4000, 3000, "bf16", (192, 256)),     # 252 tiles instead of 192
     (4000, 3000, "f16", (192, 256)),
+    # a last round that fills part of the CUs counts less than a full one for the
+    # 16-bit 256^2 and 192x256 tiles (a partly filled chip clocks higher)
+    (4608, 4608, "bf16", (192, 256)),     # 432 tiles (1.69 rounds) beat 1296 of 128^2
+    (4096, 5120, "f16", (192, 256)),      # 440 tiles (1.72 rounds)
+    (1536, 12288, "bf16", (192, 256)),    # 384 tiles (1.5 rounds)
+    (12288, 5120, "bf16", (256, 256)),    # 960 tiles (3.75 rounds) beat 1280 of 192x256
+    (8192, 8192, "bf16", (256, 256)),     # four full rounds
+    (6144, 4096, "bf16", (128, 128)),     # 1536 tiles of 128^2 (the model's pick; measured
+                                          # 192x256 ~10 % faster: a known miss)
     (512, 512, "bf16", (32, 32)),         # slice-K: 256 tiles of 32^2
     (1024, 1024, "f16", (64, 64)),        # slice-K: 256 tiles of 64^2
     (1024, 1152, "bf16", (128, 128)),     # 72 tiles of 128^2: past the 16-bit slice-K limit of 64
@@ -224,6 +233,8 @@ def test_tile_map_rejects_bad_arguments():
     (512, 512, "f32", (32, 32)),          # slice-K: 256 tiles of 32^2
     (1, 1, "f32", (32, 32)),
     (4000, 3000, "f32x3", (256, 256)),
+    (4608, 4608, "f32x3", (128, 128)),    # 3 x bf16 keeps whole rounds for its 256^2 tile
+    (4096, 5120, "f32x3", (128, 128)),
     (1024, 1152, "f32x3", (128, 128)),    # 72 tiles of 128^2: past the 3 x bf16 slice-K limit of 64
     (1024, 1024, "f32x3", (64, 64)),      # slice-K, 256 tiles of 64^2
     (768, 768, "f32x3", (64, 64)),
@@ -301,13 +312,17 @@ def test_plan_without_workspace_is_the_plain_launch(M, N, K, fmt):
     (256, 256, 8192, "f32x3", None),    # deep K: 16 splits of 128^2 beat slice-K
     (64, 64, 4096, "f16", None),
     (256, 256, 65536, "bf16", None),
+    (4608, 4096, 16384, "bf16", 2),     # split-K is weighed with whole rounds: two splits
+    (12288, 1536, 16384, "bf16", 2),    # of 192x256 measured 4-6 % faster than unsplit
 ])
 @pytest.mark.usefixtures("no_stream_k")
 def test_split_plans(M, N, K, fmt, splits):
     p = dg.gemm_ex_plan(fmt, M, N, K, 1 << 40)
-    if splits is not None:
-        assert p["splits"] == splits and p["workspace_bytes"] == 0
+    if splits == 1:
+        assert p["splits"] == 1 and p["workspace_bytes"] == 0
         return
+    if splits is not None:
+        assert p["splits"] == splits
     assert p["splits"] > 1
     ldw = -(-N // 4) * 4
     assert p["workspace_bytes"] == p["splits"] * M * ldw * 4
