@@ -15,7 +15,10 @@ product (512 x 4096 x 4096), are timed under "other_shapes", unsplit and, where
 the planner splits K, through gemm_ex with a workspace; each both launched call by
 call from Python and replayed from a HIP graph (the small shapes are otherwise
 bound by the host's launch rate).  "plan_compare" times the cost model's plan
-against a forced Stream-K plan on the shapes with fewer tiles than CUs.
+against a forced Stream-K plan on the shapes with fewer tiles than CUs;
+"plan_compare_small" the slice-K plans of small outputs against the 128 x 128
+grid kernel; "plan_compare_tiles" the cost model's unsplit tile against each
+16-bit tile forced, on outputs of one to four rounds of 256 x 256 tiles.
 
     python bench.py [--steps K] [--warmup W] [--dtype bf16|f16|f32]
                     [--no-cpu-baseline] [--no-per-dtype] [--no-shapes]
@@ -593,6 +596,60 @@ def plan_compare_small(dg, args):
     return out
 
 
+# Outputs between one and four rounds of 256 x 256 tiles: the cost model's
+# unsplit tile against each 16-bit tile forced (bf16 inputs, normal(0, 0.02),
+# bf16 C, no workspace).  6144 x 4096 x 4096 is one the model gets wrong.
+TILE_PLAN_SHAPES = [("bf16 4608^2 x 4096", 4608, 4608, 4096),
+                    ("bf16 1536x12288x4104", 1536, 12288, 4104),
+                    ("bf16 12288x5120x2048", 12288, 5120, 2048),
+                    ("bf16 6144x4096x4096", 6144, 4096, 4096)]
+
+
+def plan_compare_tiles(dg, args):
+    """Per shape: the plain launch with the cost model's tile, and with each
+    16-bit tile (256 x 256, 192 x 256, 128 x 128) forced unsplit, timed by graph
+    replay, best of two alternating passes."""
+    import torch
+    from synth_inputs import pair, to_torch, torch_dtype
+    out = []
+
+    def ex_entry(a, b, c, stream=None):
+        dg.gemm_ex(a, b, c, stream=stream)
+    try:
+        for label, M, N, K in TILE_PLAN_SHAPES:
+            A, B = pair(M, N, K, "normal002", "bf16", seed=6200)
+            Ad, Bd = to_torch(A, "bf16").to("cuda"), to_torch(B, "bf16").to("cuda")
+            Cd = torch.empty((M, N), dtype=torch_dtype("bf16"), device="cuda")
+            del A, B
+            print(f"bench: tile plans {label}", file=sys.stderr, flush=True)
+            rec = {"shape": label, "M": M, "N": N, "K": K}
+            best = {}
+            # two passes over the plans, best of each: the first timing after a
+            # change of load trails the power controller
+            for _ in range(2):
+                for key, force in (("cost_model", None), ("tile_256x256", (256, 256, 1)),
+                                   ("tile_192x256", (192, 256, 1)), ("tile_128x128", (128, 128, 1))):
+                    if force:
+                        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_GRID, *force)
+                    else:
+                        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+                    plan = dg.gemm_ex_plan("bf16", M, N, K, 0, out_same=True)
+                    for _ in range(3):
+                        ex_entry(Ad, Bd, Cd)
+                    torch.cuda.synchronize()
+                    t = min(time_graph(ex_entry, Ad, Bd, Cd, 8) for _ in range(3))
+                    best[key] = (min(t, best[key][0]) if key in best else t,
+                                 [plan["tile_rows"], plan["tile_cols"]])
+            for key, (t, tile) in best.items():
+                rec[key] = {"tile": tile, "graph_us": round(t * 1e6, 2),
+                            "tflops": round(tflops(M, N, K, t), 2)}
+            out.append(rec)
+            del Ad, Bd, Cd
+    finally:
+        dg.dgemm_set_plan_override(dg.DGEMM_PLAN_AUTO)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -722,6 +779,7 @@ def main():
     if not args.no_plans:
         line["plan_compare"] = plan_compare(dg, args)
         line["plan_compare_small"] = plan_compare_small(dg, args)
+        line["plan_compare_tiles"] = plan_compare_tiles(dg, args)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(A, B, meta)
