@@ -598,7 +598,7 @@ def plan_compare_small(dg, args):
 
 # Outputs between one and four rounds of 256 x 256 tiles: the cost model's
 # unsplit tile against each 16-bit tile forced (bf16 inputs, normal(0, 0.02),
-# bf16 C, no workspace).  6144 x 4096 x 4096 is one the model gets wrong.
+# bf16 C, no workspace).
 TILE_PLAN_SHAPES = [("bf16 4608^2 x 4096", 4608, 4608, 4096),
                     ("bf16 1536x12288x4104", 1536, 12288, 4104),
                     ("bf16 12288x5120x2048", 12288, 5120, 2048),

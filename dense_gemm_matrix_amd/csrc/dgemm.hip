@@ -125,7 +125,10 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // rounds = ceil(tiles * s / 256) workgroups per CU.  128 x 128 tiles fit two
 // workgroups on a CU: two co-resident ones take `pair` times as long as one
 // alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them rounds counts pairs and
-// the term in parentheses is multiplied by `pair`.  For the 16-bit 256 x 256
+// the term in parentheses is multiplied by `pair`; grids of two or more rounds
+// of pairs use `pair2` (bf16 1.35: 1.32-1.37 per full round of pairs on the
+// 16-bit multi-round shapes below; the same as `pair` for the other formats,
+// whose sweeps did not separate the two).  For the 16-bit 256 x 256
 // and 192 x 256 tiles a last round that fills a fraction f of the CUs counts
 // `last + (1 - last) * f` of a full round (last = 0.6): under the power cap a
 // partly filled chip runs at a higher clock, so a grid of 1.25 rounds takes
@@ -133,10 +136,9 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // the split-K choice below keeps whole rounds, as in the sweeps it was fitted
 // to (with the rule there, two K = 16384 shapes dropped a 2-way split that is
 // 4-6 % faster).  bf16, 36 shapes from 2048 x 8192 to 8192^2 at K = 2048 and
-// 4096, unsplit: the fastest of the three tiles on 32 (14 before the rule chose
-// 128 x 128 tiles 6-11 % slower than the best; the 4 left, at 6144 x 4096 and
-// 8192 x 5120, were among them); on 7 more shapes whose tile it changes, 1-16 %
-// faster.  The 3 x bf16 256 x 256 tile keeps whole rounds: its second round
+// 4096, unsplit: with both rules the fastest of the three tiles on every one
+// (before them, 14 chose 128 x 128 tiles 6-11 % slower than the best); on 15
+// more shapes whose tile they change, 1-20 % faster.  The 3 x bf16 256 x 256 tile keeps whole rounds: its second round
 // costs ~0.6 of the first whatever its fill, but its 128 x 128 tile wins anyway
 // on the shapes where a partial-round rule would pick the 256 x 256 one.  A grid of at most one
 // workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
@@ -163,18 +165,24 @@ constexpr double SPLIT_MARGIN = 0.9;      // a split plan must be predicted 10% 
 // sweep of forced plans 256 x 256 was slower at every shape (4096^3: 1049 us
 // against 1002 us), and the cost model never chose it; eff stays relative to
 // a 256 x 256 workgroup so that step_us keeps one meaning.
-// `last`: the cost of a last, partly filled round at zero fill (1: whole rounds).
-struct TileCand { int bm, bn; double eff, pair, eff1, last; };
-constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 1.0, 0.6}, {192, 256, 0.95, 0.0, 0.95, 0.6},
-                                {128, 128, 0.6, 1.26, 0.8, 1.0}};
-constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 0.85, 1.0}};
-constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 1.0, 1.0}, {128, 128, 0.5, 1.22, 0.6, 1.0}};
+// `pair2`: the pair factor of grids of two or more rounds of pairs; `last`: the
+// cost of a last, partly filled round at zero fill (1: whole rounds).
+struct TileCand { int bm, bn; double eff, pair, pair2, eff1, last; };
+constexpr TileCand TILES16[] = {{256, 256, 1.0, 0.0, 0.0, 1.0, 0.6},
+                                {192, 256, 0.95, 0.0, 0.0, 0.95, 0.6},
+                                {128, 128, 0.6, 1.26, 1.35, 0.8, 1.0}};
+constexpr TileCand TILES32[] = {{128, 128, 0.85, 1.5, 1.5, 0.85, 1.0}};
+constexpr TileCand TILES32X3[] = {{256, 256, 1.0, 0.0, 0.0, 1.0, 1.0},
+                                  {128, 128, 0.5, 1.22, 1.22, 0.6, 1.0}};
 
 // Workgroup rounds per CU for `wgs` workgroups, and the time factor of a round;
 // `partial`: price a partly filled last round by the tile's `last`.
 double rounds_factor(const TileCand& t, int64_t wgs, bool partial = false) {
     const int64_t per_cu = (wgs + NUM_CU - 1) / NUM_CU;
-    if (t.pair > 0.0 && per_cu >= 2) return (double)((per_cu + 1) / 2) * t.pair;
+    if (t.pair > 0.0 && per_cu >= 2) {
+        const int64_t pairs = (per_cu + 1) / 2;
+        return (double)pairs * (pairs >= 2 ? t.pair2 : t.pair);
+    }
     if (partial && per_cu >= 2 && t.last < 1.0) {
         const double fill = (double)(wgs - (per_cu - 1) * NUM_CU) / NUM_CU;
         return (double)(per_cu - 1) + t.last + (1.0 - t.last) * fill;
@@ -344,7 +352,7 @@ Plan slice_plan(int in, int M, int N, int K) {
 TileCand pick_tile(int in, int M, int N) {
     if (slice_eligible(in, M, N)) {
         const int ts = slice_tile(in, M, N);
-        return TileCand{ts, ts, 1.0, 0.0, 1.0, 1.0};
+        return TileCand{ts, ts, 1.0, 0.0, 0.0, 1.0, 1.0};
     }
     int n = 0;
     const TileCand* cands = tiles_for(in, n);

@@ -216,8 +216,10 @@ def test_tile_map_rejects_bad_arguments():
     (1536, 12288, "bf16", (192, 256)),    # 384 tiles (1.5 rounds)
     (12288, 5120, "bf16", (256, 256)),    # 960 tiles (3.75 rounds) beat 1280 of 192x256
     (8192, 8192, "bf16", (256, 256)),     # four full rounds
-    (6144, 4096, "bf16", (128, 128)),     # 1536 tiles of 128^2 (the model's pick; measured
-                                          # 192x256 ~10 % faster: a known miss)
+    (6144, 4096, "bf16", (192, 256)),     # two full rounds beat 1536 tiles of 128^2 (three
+                                          # rounds of pairs, each 1.35x one workgroup)
+    (8192, 5120, "bf16", (256, 256)),     # 2.5 rounds beat 2560 tiles of 128^2
+    (2048, 4096, "bf16", (128, 128)),     # 512 tiles of 128^2: one round of pairs (1.26x)
     (512, 512, "bf16", (32, 32)),         # slice-K: 256 tiles of 32^2
     (1024, 1024, "f16", (64, 64)),        # slice-K: 256 tiles of 64^2
     (1024, 1152, "bf16", (128, 128)),     # 72 tiles of 128^2: past the 16-bit slice-K limit of 64
