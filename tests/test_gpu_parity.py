@@ -244,6 +244,28 @@ def test_exact_integer_192_tile_padded_pitches(path, out):
     assert gap_untouched(C)
 
 
+@pytest.mark.parametrize("path", ["bf16", "f16"])
+@pytest.mark.parametrize("M,N,K,tile", [
+    (4608, 4608, 100, (192, 256)),    # 432 tiles: one round, then 176 (69 % of the CUs)
+    (1536, 12288, 65, (192, 256)),    # 384 tiles: one round, then 128
+    (8192, 5120, 72, (256, 256)),     # 640 tiles: two rounds, then 128
+])
+def test_exact_integer_multi_round_grids(path, M, N, K, tile):
+    """Outputs of more than one round of 192 x 256 or 256 x 256 tiles with a
+    partly filled last round (the planner's tiles for these shapes): every
+    workgroup index past the CU count maps to its own tile.  Integer inputs,
+    fp32 C and C in the input format alternately; equal to the oracle in every
+    element."""
+    tm = dg.dgemm_tile_map(M, N, path)
+    assert (tm["tile_rows"], tm["tile_cols"]) == tile
+    out = "f32" if (M + K) % 2 == 0 else path
+    print(f"case multi-round {path}->{out} {M}x{N}x{K} tile {tile}", flush=True)
+    A, B = pair(M, N, K, "ints", path, seed=3150 + K)
+    C = run(path, out, A, B, a_extra=8, b_extra=8)
+    assert_exact(C, path, out, A, B)
+    assert gap_untouched(C)
+
+
 def test_repeat_runs_are_bitwise_identical():
     A, B = pair(1024, 1024, 2048, "normal", "bf16", seed=4000)
     C1 = run("bf16", "f32", A, B)
