@@ -122,29 +122,34 @@ int validate(int M, int N, int K, const void* A, int lda, const void* B, int ldb
 // where step_us is the measured time of one K step of a 256 x 256 workgroup,
 // eff the tile's measured throughput relative to it (one workgroup per CU),
 // reduce_bytes counts the partial sums written and read back plus C, and
-// rounds = ceil(tiles * s / 256) workgroups per CU.  128 x 128 tiles fit two
-// workgroups on a CU: two co-resident ones take `pair` times as long as one
-// alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them rounds counts pairs and
-// the term in parentheses is multiplied by `pair`; grids of two or more rounds
-// of pairs use `pair2` (bf16 1.35: 1.32-1.37 per full round of pairs on the
-// 16-bit multi-round shapes below; the same as `pair` for the other formats,
-// whose sweeps did not separate the two).  For the 16-bit 256 x 256
-// and 192 x 256 tiles a last round that fills a fraction f of the CUs counts
-// `last + (1 - last) * f` of a full round (last = 0.6): under the power cap a
-// partly filled chip runs at a higher clock, so a grid of 1.25 rounds takes
-// ~1.7 times one round, not 2.  The rule picks the unsplit tile (`pick_tile`);
-// the split-K choice below keeps whole rounds, as in the sweeps it was fitted
-// to (with the rule there, two K = 16384 shapes dropped a 2-way split that is
-// 4-6 % faster).  bf16, 36 shapes from 2048 x 8192 to 8192^2 at K = 2048 and
-// 4096, unsplit: with both rules the fastest of the three tiles on every one
-// (before them, 14 chose 128 x 128 tiles 6-11 % slower than the best); on 15
-// more shapes whose tile they change, 1-20 % faster.  The 3 x bf16 256 x 256 tile keeps whole rounds: its second round
-// costs ~0.6 of the first whatever its fill, but its 128 x 128 tile wins anyway
-// on the shapes where a partial-round rule would pick the 256 x 256 one.  A grid of at most one
+// rounds = ceil(tiles * s / 256) workgroups per CU.  A grid of at most one
 // workgroup per CU uses `eff1` in place of eff: the 16-bit 128 x 128 tile then
 // runs with a deeper LDS ring (4 stages), which only fits one workgroup per CU,
 // and the 3 x bf16 one is measured faster alone on its CU than its pair factor
 // implies.
+//
+// 128 x 128 tiles fit two workgroups on a CU: two co-resident ones take `pair`
+// times as long as one alone (bf16 1.26, fp32 1.5, 3 x bf16 1.22), so for them
+// rounds counts pairs and the term in parentheses is multiplied by `pair`.
+// Grids of two or more rounds of pairs use `pair2`: for 16-bit inputs 1.35 (a
+// full round of pairs measured 1.32-1.37 on the multi-round shapes below); for
+// the other formats the same as `pair`, their sweeps not separating the two.
+//
+// Partly filled last rounds (16-bit 256 x 256 and 192 x 256 tiles): a last
+// round that fills a fraction f of the CUs counts `last + (1 - last) * f` of a
+// full round, last = 0.6.  Under the power cap a partly filled chip runs at a
+// higher clock, so a grid of 1.25 rounds takes ~1.7 times one round, not 2.
+// The rule prices the unsplit tile choice (`pick_tile`) only; the split-K
+// choice keeps whole rounds, as in the sweeps it was fitted to (with the rule
+// there, two K = 16384 shapes dropped a 2-way split that is 4-6 % faster).
+// Measured on 36 unsplit bf16 shapes from 2048 x 8192 to 8192^2 at K = 2048
+// and 4096: with `pair2` and this rule the planner picks the fastest of the
+// three tiles on every one (before them, 14 chose 128 x 128 tiles 6-11 %
+// slower than the best); on 15 more shapes whose tile they change, the new
+// tile is 1-20 % faster.  The 3 x bf16 256 x 256 tile keeps whole rounds: its
+// second round costs ~0.6 of the first whatever its fill, but on the shapes
+// where a partial-round rule would pick it, its 128 x 128 tile is as fast.
+//
 // A grid of fewer tiles than CUs, or K much deeper than M and N, is where
 // splitting pays (the nine-levels tutorial's section 2.9 names Split-K for
 // small-matrix parallelism); everywhere else the unsplit plan wins.  The
