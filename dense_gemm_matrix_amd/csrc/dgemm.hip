@@ -255,21 +255,28 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // kept the deepest shapes when a workspace is offered (256 x 256 x 8192 3 x bf16
 // 25.5 against 40 us).
 
-struct SliceCand { int ts, waves; double fixed_us, blk_us, co, round_us; };
+// fill_us: the per-block cost added at a full round, in proportion to the
+// fraction of the CUs the grid fills (0: none measured).
+struct SliceCand { int ts, waves; double fixed_us, blk_us, co, round_us, fill_us; };
 // fp32 matrix instruction: 32 x 32 with 4 or 8 waves, 64 x 64 with 4.
-constexpr SliceCand SLICE_F32[] = {{32, 4, 2.4, 0.9, 0.82, 0.1},
-                                   {32, 8, 2.7, 1.35, 1.0, 1.6},
-                                   {64, 4, 3.7, 2.27, 1.0, 4.6}};
+constexpr SliceCand SLICE_F32[] = {{32, 4, 2.4, 0.9, 0.82, 0.1, 0.0},
+                                   {32, 8, 2.7, 1.35, 1.0, 1.6, 0.0},
+                                   {64, 4, 3.7, 2.27, 1.0, 4.6, 0.0}};
 // 3 x bf16: the same tiles.
-constexpr SliceCand SLICE_X3[] = {{32, 4, 2.4, 0.72, 0.86, 0.1},
-                                  {32, 8, 2.5, 1.19, 1.0, 1.6},
-                                  {64, 4, 3.6, 1.28, 1.04, 2.9}};
+constexpr SliceCand SLICE_X3[] = {{32, 4, 2.4, 0.72, 0.86, 0.1, 0.0},
+                                  {32, 8, 2.5, 1.19, 1.0, 1.6, 0.0},
+                                  {64, 4, 3.6, 1.28, 1.04, 2.9, 0.0}};
 // bf16 / fp16 (blocks of 64 k): the same tiles; 8 waves were never faster
 // than 4 in the sweep (the 64 x 64 tile's rounds are not fitted: at most 64
-// tiles of 128 x 128 give it one round).
-constexpr SliceCand SLICE_16[] = {{32, 4, 2.45, 0.60, 1.04, 0.6},
-                                  {32, 8, 2.45, 1.22, 1.08, 1.4},
-                                  {64, 4, 3.0, 1.14, 1.0, 2.9}};
+// tiles of 128 x 128 give it one round).  The 64 x 64 tile's cost per block
+// rises with the grid's fill: 1.08-1.18 us at 64-128 workgroups, 1.14-1.16 at
+// 192, 1.18-1.27 at 256 (a full chip clocks lower), so 1.08 + 0.15 * fill.
+// With the flat 1.14 it kept 1024 x 1024 x 4096, 512 x 2048 x 4096 and
+// 256 x 4096 x 4096 on slice-K (23.3 us) when 4 splits of 128 x 128 tiles
+// take 19.8.
+constexpr SliceCand SLICE_16[] = {{32, 4, 2.45, 0.60, 1.04, 0.6, 0.0},
+                                  {32, 8, 2.45, 1.22, 1.08, 1.4, 0.0},
+                                  {64, 4, 3.0, 1.08, 1.0, 2.9, 0.15}};
 
 bool slice_format(int in) { (void)in; return true; }
 
@@ -302,10 +309,18 @@ int64_t slice_per_cu(const SliceCand& c, int M, int N) {
 
 double slice_load(const SliceCand& c, int64_t n) { return n == 1 ? 1.0 : (double)n * c.co; }
 
+// Cost per block of K of one wave, at the grid's fill of the CUs.
+double slice_blk(const SliceCand& c, int M, int N) {
+    const int64_t tiles = ceil_div(M, c.ts) * ceil_div(N, c.ts);
+    const double fill = tiles >= NUM_CU ? 1.0 : (double)tiles / NUM_CU;
+    return c.blk_us + c.fill_us * fill;
+}
+
 double estimate_slice_us(int in, const SliceCand& c, int M, int N, int K) {
     const int64_t n = slice_per_cu(c, M, N);
     const int64_t nbw = ceil_div(ceil_div(K, slice_bk(in)), c.waves);
-    return c.fixed_us + (double)nbw * c.blk_us * slice_load(c, n) + (double)(n - 1) * c.round_us;
+    return c.fixed_us + (double)nbw * slice_blk(c, M, N) * slice_load(c, n) +
+           (double)(n - 1) * c.round_us;
 }
 
 // The candidate of format `in` with tile ts and `waves` waves (nullptr: none).
@@ -323,8 +338,8 @@ const SliceCand* slice_cand(int in, int ts, int waves) {
 int slice_tile(int in, int M, int N) {
     const SliceCand& c32 = *slice_cand(in, 32, 4);
     const SliceCand& c64 = *slice_cand(in, 64, 4);
-    return c32.blk_us * slice_load(c32, slice_per_cu(c32, M, N)) <=
-                   c64.blk_us * slice_load(c64, slice_per_cu(c64, M, N))
+    return slice_blk(c32, M, N) * slice_load(c32, slice_per_cu(c32, M, N)) <=
+                   slice_blk(c64, M, N) * slice_load(c64, slice_per_cu(c64, M, N))
                ? 32
                : 64;
 }

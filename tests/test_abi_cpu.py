@@ -314,6 +314,9 @@ def test_plan_without_workspace_is_the_plain_launch(M, N, K, fmt):
     (256, 256, 8192, "f32x3", None),    # deep K: 16 splits of 128^2 beat slice-K
     (64, 64, 4096, "f16", None),
     (256, 256, 65536, "bf16", None),
+    (1024, 1024, 2048, "bf16", 1),      # slice-K (12.5 us) beats every split (16.8 us best)
+    (1024, 1024, 4104, "bf16", 4),      # full 64x64 slice-K grid: its per-block cost grows
+    (512, 2048, 4104, "bf16", 4),       # with the fill, and 4 splits measure 10-16 % faster
     (4608, 4096, 16384, "bf16", 2),     # split-K is weighed with whole rounds: two splits
     (12288, 1536, 16384, "bf16", 2),    # of 192x256 measured 4-6 % faster than unsplit
 ])
