@@ -187,7 +187,8 @@ typedef enum {
  * no workspace and no second kernel, deterministic for a given shape.  Offered
  * a workspace, the planner compares this plan with the split plans by their
  * estimated times and takes a split plan only when it is estimated at least
- * 10 % faster (deep K on few tiles).
+ * 10 % faster: deep K on few tiles and, for bf16 / fp16, outputs that fill the
+ * CUs with 64 x 64 tiles at K of about 4096 and more.
  *
  * Stream-K (the nine-levels tutorial, section 2.9: the refinement of Split-K
  * that gives every thread block the same amount of work): for bf16 / fp16
